@@ -1,0 +1,229 @@
+"""CPU oracle for speculative-verification attention and verify-set selection.
+
+TEST INFRASTRUCTURE ONLY.  Only the test-suite, the package smoke check and
+the benchmark's CPU-baseline leg may import this module.  The HIP library
+never calls it and shares no code with it.
+
+Everything is plain numpy in float64, written for a reader to check against
+the pages by eye:
+
+* ``verify_attention`` is the plain definition of what the hybrid tree
+  attention computes (LongSpec, "Tree Attention Ibrida"): each draft node
+  attends, with no mask, to every context key (the whole cache, or the
+  verify subset of Dustin, "Workflow di Verifica" steps 3-4), and, under the
+  tree mask, to itself and its ancestors among the draft nodes.  The page
+  splits the two parts and re-joins them with a log-sum-exp merge; that merge
+  is exact, so its result is the single softmax over the concatenated key set
+  that is written out here.  No split, no merge, no blocking.
+* ``select_verify_set`` follows the selection rule of Dustin, "Metodologia"
+  section 1 (Aggregazione Ibrida dell'Attenzione): protect an attention-sink
+  prefix and a local window of recent tokens, then fill the remaining budget
+  with the top-m tokens by the draft-lookahead score, then the most relevant
+  remaining tokens by the target-historical score.  It is written with a
+  stable sort.
+
+Readings where the pages are silent (each listed with its reason in the
+design notes of the repository):
+
+* softmax scale 1/sqrt(D); query head h reads KV head h // (Hq // Hkv);
+* ``parent[i] == -1`` means node i hangs off the last committed token, which
+  is already in the context; ``parent[i] < i`` (topological order);
+* the verify set restricts the context part only, the draft part is always
+  complete; the budget counts the sink and the window; sink and window are a
+  union; the draft tier takes min(m, remaining budget, remaining tokens);
+* ties in a score go to the lower token index; NaN ranks below -inf, and
+  -0 equals +0; the output index list is ascending;
+* ``lse`` is the natural-log log-sum-exp of the scaled scores of a row.
+
+Parity status: every function here is pinned by the ``-m "not gpu"`` tests
+(closed forms, textbook special cases, brute force); none is "parity
+unpinned".
+"""
+
+from __future__ import annotations
+
+from typing import Iterable, Optional, Sequence, Tuple
+
+import numpy as np
+
+
+# ---------------------------------------------------------------------------
+# inputs
+
+
+def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    """bfloat16 bit patterns (uint16) -> exact float64 values."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16
+    return b.view(np.float32).astype(np.float64)
+
+
+def as_f64(x: np.ndarray) -> np.ndarray:
+    """Exact float64 view of an input tensor (bf16 bits or float32)."""
+    x = np.asarray(x)
+    if x.dtype == np.uint16:
+        return bf16_bits_to_f64(x)
+    return x.astype(np.float64)
+
+
+# ---------------------------------------------------------------------------
+# tree mask (LongSpec "Tree Attention Ibrida": the speculative part needs the
+# tree mask; BASTION "Drafting a Diffusione a Blocchi Basato su Albero": the
+# candidates form a prefix tree)
+
+
+def ancestor_mask(parent: Sequence[int]) -> np.ndarray:
+    """anc[i, j] is True when draft node j is node i or one of its ancestors.
+
+    Built by walking each node's parent chain up to the virtual root (-1).
+    """
+    parent = [int(p) for p in parent]
+    n = len(parent)
+    anc = np.zeros((n, n), dtype=bool)
+    for i in range(n):
+        if not -1 <= parent[i] < i:
+            raise ValueError(f"parent[{i}] = {parent[i]} breaks -1 <= parent[i] < i")
+        j = i
+        while j != -1:
+            anc[i, j] = True
+            j = parent[j]
+    return anc
+
+
+# ---------------------------------------------------------------------------
+# attention
+
+
+def masked_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray,
+                     mask: np.ndarray, scale: float) -> Tuple[np.ndarray, np.ndarray]:
+    """Softmax attention of rows q[R, D] over keys k[C, D] / values v[C, D].
+
+    mask[R, C] marks the keys each row may see.  One softmax per row over all
+    its visible keys, max-subtracted.  Returns (out[R, D], lse[R]) with
+    lse = ln(sum_j exp(s_j)) over the visible keys.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    mask = np.asarray(mask, dtype=bool)
+    if not mask.any(axis=1).all():
+        raise ValueError("a row sees no key")
+    s = scale * (q @ k.T)
+    s = np.where(mask, s, -np.inf)
+    m = s.max(axis=1, keepdims=True)
+    p = np.exp(s - m)
+    l = p.sum(axis=1, keepdims=True)
+    out = (p @ v) / l
+    lse = m[:, 0] + np.log(l[:, 0])
+    return out, lse
+
+
+def default_scale(D: int) -> float:
+    return 1.0 / np.sqrt(D)
+
+
+def verify_attention(q, k_cache, v_cache, k_draft, v_draft, parent,
+                     scale: Optional[float] = None,
+                     ctx_index: Optional[np.ndarray] = None,
+                     heads: Optional[Iterable[Tuple[int, int]]] = None):
+    """Verification attention of N draft nodes against the target KV cache.
+
+    Shapes: q [B, Hq, N, D]; k_cache, v_cache [B, Hkv, L, D];
+    k_draft, v_draft [B, Hkv, N, D]; parent [B, N] int.  Inputs may be bf16
+    bit patterns (uint16) or floats; they are upcast exactly to float64.
+
+    ctx_index [B, K]: when given, sequence b's context part is the key set
+    {ctx_index[b, :]} (Dustin's verify set, read from the full cache in place)
+    instead of the whole cache [0, L).
+
+    heads: optional (b, h) pairs; then only those are computed and the result
+    is (out[len(heads), N, D], lse[len(heads), N]).  Otherwise the result is
+    (out[B, Hq, N, D], lse[B, Hq, N]).
+    """
+    B, Hq, N, D = q.shape
+    Hkv = k_cache.shape[1]
+    if Hq % Hkv:
+        raise ValueError("Hq must be a multiple of Hkv")
+    G = Hq // Hkv
+    L = k_cache.shape[2]
+    sc = default_scale(D) if scale is None else float(scale)
+    pairs = list(heads) if heads is not None else [(b, h) for b in range(B) for h in range(Hq)]
+
+    outs = np.empty((len(pairs), N, D), dtype=np.float64)
+    lses = np.empty((len(pairs), N), dtype=np.float64)
+    anc_cache = {}
+    kv_cache = {}
+    for n, (b, h) in enumerate(pairs):
+        if b not in anc_cache:
+            anc_cache[b] = ancestor_mask(parent[b])
+        anc = anc_cache[b]
+        kv = h // G
+        if (b, kv) not in kv_cache:
+            kv_cache.clear()
+            if ctx_index is None:
+                pos = np.arange(L)
+            else:
+                pos = np.unique(np.asarray(ctx_index[b], dtype=np.int64))
+                if pos.size and (pos[0] < 0 or pos[-1] >= L):
+                    raise ValueError("ctx_index out of range")
+            keys = np.concatenate([as_f64(k_cache[b, kv][pos]), as_f64(k_draft[b, kv])])
+            vals = np.concatenate([as_f64(v_cache[b, kv][pos]), as_f64(v_draft[b, kv])])
+            kv_cache[(b, kv)] = (pos.size, keys, vals)
+        C, keys, vals = kv_cache[(b, kv)]
+        mask = np.concatenate([np.ones((N, C), dtype=bool), anc], axis=1)
+        o, l = masked_attention(as_f64(q[b, h]), keys, vals, mask, sc)
+        outs[n] = o
+        lses[n] = l
+    if heads is not None:
+        return outs, lses
+    return outs.reshape(B, Hq, N, D), lses.reshape(B, Hq, N)
+
+
+# ---------------------------------------------------------------------------
+# verify-set selection (Dustin, "Aggregazione Ibrida dell'Attenzione")
+
+
+def _rank_order(score: np.ndarray, cand: np.ndarray) -> np.ndarray:
+    """Candidates sorted best first: higher score first, lower index on ties.
+
+    NaN ranks below every number (also below -inf); -0 and +0 are equal.
+    """
+    s = np.asarray(score, dtype=np.float64)[cand]
+    is_num = ~np.isnan(s)
+    val = np.where(is_num, s, 0.0) + 0.0    # + 0.0 turns -0 into +0
+    # np.lexsort sorts by the last key first, ascending.
+    order = np.lexsort((cand, -val, ~is_num))
+    return cand[order]
+
+
+def protected_set(L: int, sink: int, window: int) -> np.ndarray:
+    """Attention-sink prefix [0, sink) united with the local window [L-window, L)."""
+    sink_part = np.arange(0, min(max(sink, 0), L))
+    win_part = np.arange(max(0, L - max(window, 0)), L)
+    return np.union1d(sink_part, win_part).astype(np.int64)
+
+
+def select_row(draft: np.ndarray, target: np.ndarray, sink: int, window: int,
+               top_m: int, budget: int) -> np.ndarray:
+    L = draft.shape[0]
+    if budget >= L:
+        return np.arange(L, dtype=np.int64)
+    prot = protected_set(L, sink, window)
+    if budget < prot.size:
+        raise ValueError("budget smaller than sink + window")
+    rest_budget = budget - prot.size
+    free = np.setdiff1d(np.arange(L), prot)
+    m = min(max(top_m, 0), rest_budget, free.size)
+    by_draft = _rank_order(draft, free)[:m]
+    remaining = np.setdiff1d(free, by_draft)
+    by_target = _rank_order(target, remaining)[:rest_budget - m]
+    return np.sort(np.concatenate([prot, by_draft, by_target]))
+
+
+def select_verify_set(draft_score: np.ndarray, target_score: np.ndarray,
+                      sink: int, window: int, top_m: int, budget: int) -> np.ndarray:
+    """I_verify per sequence: int64 [B, min(budget, L)], ascending."""
+    draft_score = np.asarray(draft_score)
+    target_score = np.asarray(target_score)
+    rows = [select_row(draft_score[b], target_score[b], sink, window, top_m, budget)
+            for b in range(draft_score.shape[0])]
+    return np.stack(rows) if rows else np.zeros((0, 0), dtype=np.int64)

@@ -1,0 +1,508 @@
+"""Pins for the CPU oracle: each checks it against something other than itself.
+
+Attention pins: textbook special cases computed by torch's scaled-dot-product
+attention and logsumexp (float64, CPU), closed forms, and an LSE-merge
+identity.  Selector pins: a brute-force counting definition of "top-r with
+ties to the lower index", special cases named on the pages, and a
+hand-derived example.  The tree mask is pinned against a transitive closure
+and a hand-derived example.
+"""
+
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+from hypothesis import given, settings, strategies as st
+
+from oracle import verify_oracle as vo
+from long_context_verify_tree_amd import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def rand_inputs(rng, B, Hq, Hkv, N, D, L, tree="uniform"):
+    q = rng.standard_normal((B, Hq, N, D))
+    kc = rng.standard_normal((B, Hkv, L, D))
+    vc = rng.standard_normal((B, Hkv, L, D))
+    kd = rng.standard_normal((B, Hkv, N, D))
+    vd = rng.standard_normal((B, Hkv, N, D))
+    if tree == "chain":
+        parent = np.stack([synth.chain_parents(N)] * B)
+    elif tree == "star":
+        parent = np.full((B, N), -1, dtype=np.int32)
+    else:
+        parent = np.stack([synth.uniform_parents(rng, N) for _ in range(B)])
+    return q, kc, vc, kd, vd, parent
+
+
+def sdpa(q, k, v, mask=None):
+    """torch's attention (float64, CPU) with an optional boolean mask."""
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float64))
+    m = None if mask is None else torch.from_numpy(np.asarray(mask, dtype=bool))
+    return torch.nn.functional.scaled_dot_product_attention(
+        t(q)[None], t(k)[None], t(v)[None], attn_mask=m)[0].numpy()
+
+
+def torch_lse(q, k, scale, mask=None):
+    s = torch.from_numpy(np.asarray(q, np.float64)) @ torch.from_numpy(np.asarray(k, np.float64)).T
+    s = s * scale
+    if mask is not None:
+        s = s.masked_fill(~torch.from_numpy(np.asarray(mask, dtype=bool)), float("-inf"))
+    return torch.logsumexp(s, dim=1).numpy()
+
+
+# ---------------------------------------------------------------------------
+# tree mask
+
+
+def test_ancestor_mask_hand_example():
+    g = json.load(open(os.path.join(GOLDEN, "tree_hand_example.json")))
+    anc = vo.ancestor_mask(g["parent"])
+    for i, vis in enumerate(g["visible"]):
+        assert sorted(np.nonzero(anc[i])[0].tolist()) == vis
+
+
+def test_ancestor_mask_chain_is_lower_triangular():
+    for n in (1, 2, 8, 33):
+        np.testing.assert_array_equal(vo.ancestor_mask(synth.chain_parents(n)),
+                                      np.tril(np.ones((n, n), dtype=bool)))
+
+
+def test_ancestor_mask_star_is_identity():
+    np.testing.assert_array_equal(vo.ancestor_mask([-1] * 9), np.eye(9, dtype=bool))
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_ancestor_mask_is_reflexive_transitive_closure(seed):
+    rng = np.random.default_rng(seed)
+    n = int(rng.integers(1, 40))
+    parent = (synth.uniform_parents(rng, n) if seed % 2 else
+              synth.prefix_tree_parents(rng, n, 5, 3))
+    # child -> parent adjacency, closed under composition by repeated squaring
+    adj = np.eye(n, dtype=bool)
+    for i, p in enumerate(parent):
+        if p >= 0:
+            adj[i, p] = True
+    clo = adj.copy()
+    for _ in range(int(math.ceil(math.log2(max(n, 2)))) + 1):
+        clo = (clo.astype(np.int64) @ clo.astype(np.int64)) > 0
+    np.testing.assert_array_equal(vo.ancestor_mask(parent), clo)
+
+
+def test_ancestor_mask_rejects_non_topological():
+    with pytest.raises(ValueError):
+        vo.ancestor_mask([-1, 1])
+    with pytest.raises(ValueError):
+        vo.ancestor_mask([0])
+
+
+def test_prefix_tree_generator_bounds():
+    rng = np.random.default_rng(3)
+    for N, dmax, bmax in ((64, 8, 4), (128, 12, 4)):
+        p = synth.prefix_tree_parents(rng, N, dmax, bmax)
+        anc = vo.ancestor_mask(p)
+        assert anc.sum(axis=1).max() <= dmax
+        kids = np.bincount(p[p >= 0], minlength=N)
+        assert kids.max() <= bmax and (p == -1).sum() <= bmax
+
+
+# ---------------------------------------------------------------------------
+# attention primitive
+
+
+def test_masked_attention_matches_torch_sdpa():
+    rng = np.random.default_rng(0)
+    q, k, v = rng.standard_normal((7, 16)), rng.standard_normal((23, 16)), rng.standard_normal((23, 16))
+    mask = rng.random((7, 23)) < 0.6
+    mask[:, 0] = True
+    out, lse = vo.masked_attention(q, k, v, mask, 1 / math.sqrt(16))
+    np.testing.assert_allclose(out, sdpa(q, k, v, mask), rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(lse, torch_lse(q, k, 1 / math.sqrt(16), mask), rtol=1e-13)
+
+
+def test_masked_attention_uniform_keys_closed_form():
+    # every key equal: weights are uniform over the visible keys
+    rng = np.random.default_rng(1)
+    D = 8
+    q = rng.standard_normal((3, D))
+    key = rng.standard_normal(D)
+    k = np.tile(key, (10, 1))
+    v = rng.standard_normal((10, D))
+    mask = np.zeros((3, 10), dtype=bool)
+    mask[0, :] = True
+    mask[1, [2, 5]] = True
+    mask[2, 7] = True
+    sc = 0.3
+    out, lse = vo.masked_attention(q, k, v, mask, sc)
+    for r in range(3):
+        vis = mask[r]
+        np.testing.assert_allclose(out[r], v[vis].mean(axis=0), rtol=1e-12, atol=1e-14)
+        assert lse[r] == pytest.approx(sc * q[r] @ key + math.log(vis.sum()), rel=1e-13)
+
+
+def test_masked_attention_two_keys_is_logistic():
+    q = np.array([[1.0, 0.0]])
+    k = np.array([[2.0, 0.0], [0.0, 5.0]])
+    v = np.array([[1.0, 0.0], [0.0, 1.0]])
+    out, lse = vo.masked_attention(q, k, v, np.ones((1, 2), bool), 0.5)
+    w0 = 1.0 / (1.0 + math.exp(-1.0))            # scores 1.0 and 0.0
+    assert out[0, 0] == pytest.approx(w0, rel=1e-14)
+    assert out[0, 1] == pytest.approx(1 - w0, rel=1e-14)
+    assert lse[0] == pytest.approx(math.log(math.e + 1.0), rel=1e-14)
+
+
+def test_masked_attention_rejects_empty_row():
+    with pytest.raises(ValueError):
+        vo.masked_attention(np.ones((1, 2)), np.ones((1, 2)), np.ones((1, 2)),
+                            np.zeros((1, 1), bool), 1.0)
+
+
+# ---------------------------------------------------------------------------
+# verify attention: special cases that reduce to textbook routines
+
+
+@pytest.mark.parametrize("L", [0, 1, 37])
+def test_chain_tree_equals_causal_attention(L):
+    rng = np.random.default_rng(10 + L)
+    B, Hq, Hkv, N, D = 2, 4, 2, 6, 16
+    q, kc, vc, kd, vd, parent = rand_inputs(rng, B, Hq, Hkv, N, D, L, tree="chain")
+    out, lse = vo.verify_attention(q, kc, vc, kd, vd, parent)
+    for b in range(B):
+        for h in range(Hq):
+            kv = h // (Hq // Hkv)
+            seq_k = np.concatenate([kc[b, kv], kd[b, kv]])
+            seq_v = np.concatenate([vc[b, kv], vd[b, kv]])
+            # causal attention of the last N positions of the sequence [ctx; drafts]
+            causal = np.tril(np.ones((L + N, L + N), dtype=bool))[L:]
+            np.testing.assert_allclose(out[b, h], sdpa(q[b, h], seq_k, seq_v, causal),
+                                       rtol=1e-11, atol=1e-12)
+            np.testing.assert_allclose(lse[b, h], torch_lse(q[b, h], seq_k, 1 / math.sqrt(D), causal),
+                                       rtol=1e-12, atol=1e-12)
+
+
+def test_chain_tree_equals_per_position_decode():
+    # a chain of N drafts is N ordinary decode steps over a growing prefix
+    rng = np.random.default_rng(11)
+    q, kc, vc, kd, vd, parent = rand_inputs(rng, 1, 2, 1, 5, 8, 19, tree="chain")
+    out, _ = vo.verify_attention(q, kc, vc, kd, vd, parent)
+    for i in range(5):
+        k = np.concatenate([kc[0, 0], kd[0, 0, :i + 1]])
+        v = np.concatenate([vc[0, 0], vd[0, 0, :i + 1]])
+        np.testing.assert_allclose(out[0, 1, i], sdpa(q[0, 1, i:i + 1], k, v)[0], rtol=1e-11, atol=1e-12)
+
+
+def test_single_node_is_decode():
+    rng = np.random.default_rng(12)
+    q, kc, vc, kd, vd, parent = rand_inputs(rng, 2, 8, 2, 1, 32, 50)
+    out, lse = vo.verify_attention(q, kc, vc, kd, vd, parent)
+    for b in range(2):
+        for h in range(8):
+            k = np.concatenate([kc[b, h // 4], kd[b, h // 4]])
+            v = np.concatenate([vc[b, h // 4], vd[b, h // 4]])
+            np.testing.assert_allclose(out[b, h], sdpa(q[b, h], k, v), rtol=1e-11, atol=1e-12)
+            np.testing.assert_allclose(lse[b, h], torch_lse(q[b, h], k, 1 / math.sqrt(32)), rtol=1e-12)
+
+
+def test_pure_star_tree_is_own_value():
+    rng = np.random.default_rng(13)
+    q, kc, vc, kd, vd, parent = rand_inputs(rng, 2, 4, 2, 7, 16, 0, tree="star")
+    out, lse = vo.verify_attention(q, kc, vc, kd, vd, parent)
+    for b in range(2):
+        for h in range(4):
+            np.testing.assert_array_equal(out[b, h], vd[b, h // 2])
+            np.testing.assert_allclose(lse[b, h], np.einsum("nd,nd->n", q[b, h], kd[b, h // 2]) / 4.0,
+                                       rtol=1e-14)
+
+
+def test_gqa_mapping_matches_replicated_heads():
+    # query head h reads KV head h // G: replicating each KV head G times must not change anything
+    rng = np.random.default_rng(14)
+    q, kc, vc, kd, vd, parent = rand_inputs(rng, 2, 6, 2, 4, 8, 21)
+    out, lse = vo.verify_attention(q, kc, vc, kd, vd, parent)
+    rep = lambda a: np.repeat(a, 3, axis=1)
+    out2, lse2 = vo.verify_attention(q, rep(kc), rep(vc), rep(kd), rep(vd), parent)
+    np.testing.assert_array_equal(out, out2)
+    np.testing.assert_array_equal(lse, lse2)
+    # and differs from the interleaved reading h % Hkv
+    tile = lambda a: np.tile(a, (1, 3, 1, 1))
+    out3, _ = vo.verify_attention(q, tile(kc), tile(vc), tile(kd), tile(vd), parent)
+    assert not np.allclose(out, out3)
+
+
+def test_scale_argument():
+    rng = np.random.default_rng(15)
+    q, kc, vc, kd, vd, parent = rand_inputs(rng, 1, 2, 1, 3, 8, 9)
+    out, lse = vo.verify_attention(q, kc, vc, kd, vd, parent, scale=0.7)
+    out2, lse2 = vo.verify_attention(q * (0.7 * math.sqrt(8)), kc, vc, kd, vd, parent)
+    np.testing.assert_allclose(out, out2, rtol=1e-12)
+    np.testing.assert_allclose(lse, lse2, rtol=1e-12)
+
+
+def test_tree_mask_matches_sdpa_over_concatenation():
+    rng = np.random.default_rng(16)
+    q, kc, vc, kd, vd, parent = rand_inputs(rng, 1, 2, 1, 12, 8, 30)
+    out, _ = vo.verify_attention(q, kc, vc, kd, vd, parent)
+    # mask written from the hand-walked paths of a transitive closure
+    n = 12
+    vis = np.eye(n, dtype=bool)
+    for i in range(n):
+        for j in range(n):
+            p = parent[0, i]
+            while p != -1:
+                if p == j:
+                    vis[i, j] = True
+                p = parent[0, p]
+    mask = np.concatenate([np.ones((n, 30), bool), vis], axis=1)
+    ref = sdpa(q[0, 1], np.concatenate([kc[0, 0], kd[0, 0]]), np.concatenate([vc[0, 0], vd[0, 0]]), mask)
+    np.testing.assert_allclose(out[0, 1], ref, rtol=1e-11, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# log-sum-exp merge: partial results over a split of the keys recombine exactly
+
+
+def _merge(parts):
+    """Log-sum-exp merge of (out_s, lse_s) pairs; an empty part has lse -inf."""
+    lses = np.stack([l for _, l in parts])          # [S, R]
+    M = lses.max(axis=0)
+    w = np.exp(lses - M)
+    tot = w.sum(axis=0)
+    out = sum(w[s][:, None] * parts[s][0] for s in range(len(parts))) / tot[:, None]
+    return out, M + np.log(tot)
+
+
+@pytest.mark.parametrize("n_split", [1, 2, 7, 40])
+def test_lse_merge_equals_single_softmax(n_split):
+    rng = np.random.default_rng(20 + n_split)
+    R, C, D = 5, 40, 16
+    q, k, v = rng.standard_normal((R, D)), rng.standard_normal((C, D)), rng.standard_normal((C, D))
+    full_out, full_lse = vo.masked_attention(q, k, v, np.ones((R, C), bool), 0.25)
+    bounds = np.linspace(0, C, n_split + 1).astype(int)
+    parts = []
+    for s in range(n_split):
+        a, z = bounds[s], bounds[s + 1]
+        if z == a:
+            parts.append((np.zeros((R, D)), np.full(R, -np.inf)))
+            continue
+        parts.append(vo.masked_attention(q, k[a:z], v[a:z], np.ones((R, z - a), bool), 0.25))
+    parts.append((np.zeros((R, D)), np.full(R, -np.inf)))   # an empty split
+    out, lse = _merge(parts)
+    np.testing.assert_allclose(out, full_out, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(lse, full_lse, rtol=1e-14)
+
+
+def test_context_plus_tree_merge_equals_verify():
+    # LongSpec's decomposition: unmasked context part + tree-masked part, merged by LSE
+    rng = np.random.default_rng(30)
+    q, kc, vc, kd, vd, parent = rand_inputs(rng, 1, 2, 1, 9, 16, 25)
+    out, lse = vo.verify_attention(q, kc, vc, kd, vd, parent)
+    anc = vo.ancestor_mask(parent[0])
+    for h in range(2):
+        ctx = vo.masked_attention(q[0, h], kc[0, 0], vc[0, 0], np.ones((9, 25), bool), 0.25)
+        tree = vo.masked_attention(q[0, h], kd[0, 0], vd[0, 0], anc, 0.25)
+        m_out, m_lse = _merge([ctx, tree])
+        np.testing.assert_allclose(out[0, h], m_out, rtol=1e-12, atol=1e-14)
+        np.testing.assert_allclose(lse[0, h], m_lse, rtol=1e-13)
+
+
+# ---------------------------------------------------------------------------
+# sparse verification (Dustin: the verify set is read from the full cache)
+
+
+def test_sparse_all_indices_equals_dense():
+    rng = np.random.default_rng(40)
+    q, kc, vc, kd, vd, parent = rand_inputs(rng, 2, 4, 2, 5, 8, 33)
+    idx = np.tile(np.arange(33), (2, 1))
+    d_out, d_lse = vo.verify_attention(q, kc, vc, kd, vd, parent)
+    s_out, s_lse = vo.verify_attention(q, kc, vc, kd, vd, parent, ctx_index=idx)
+    np.testing.assert_array_equal(d_out, s_out)
+    np.testing.assert_array_equal(d_lse, s_lse)
+
+
+def test_sparse_equals_dense_on_subset_cache():
+    rng = np.random.default_rng(41)
+    q, kc, vc, kd, vd, parent = rand_inputs(rng, 2, 4, 2, 5, 8, 60)
+    idx = np.stack([np.sort(rng.choice(60, 17, replace=False)) for _ in range(2)])
+    s_out, s_lse = vo.verify_attention(q, kc, vc, kd, vd, parent, ctx_index=idx)
+    sub = lambda a: np.stack([a[b][:, idx[b]] for b in range(2)])
+    d_out, d_lse = vo.verify_attention(q, sub(kc), sub(vc), kd, vd, parent)
+    np.testing.assert_allclose(s_out, d_out, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(s_lse, d_lse, rtol=1e-13)
+
+
+def test_context_order_invariance():
+    rng = np.random.default_rng(42)
+    q, kc, vc, kd, vd, parent = rand_inputs(rng, 1, 2, 1, 4, 8, 50)
+    perm = rng.permutation(50)
+    out, lse = vo.verify_attention(q, kc, vc, kd, vd, parent)
+    out2, lse2 = vo.verify_attention(q, kc[:, :, perm], vc[:, :, perm], kd, vd, parent)
+    np.testing.assert_allclose(out, out2, rtol=1e-11, atol=1e-13)
+    np.testing.assert_allclose(lse, lse2, rtol=1e-13)
+
+
+def test_heads_subset_matches_full():
+    rng = np.random.default_rng(43)
+    q, kc, vc, kd, vd, parent = rand_inputs(rng, 2, 4, 2, 3, 8, 20)
+    out, lse = vo.verify_attention(q, kc, vc, kd, vd, parent)
+    pairs = [(1, 3), (0, 0), (1, 1)]
+    o2, l2 = vo.verify_attention(q, kc, vc, kd, vd, parent, heads=pairs)
+    for n, (b, h) in enumerate(pairs):
+        np.testing.assert_array_equal(o2[n], out[b, h])
+        np.testing.assert_array_equal(l2[n], lse[b, h])
+
+
+def test_float32_torch_agrees_on_generated_bf16_config():
+    cfg = synth.small_variant(synth.CONFIGS["llama3_8b_tree64_L64k"], L=300, B=1)
+    x = synth.make_inputs(cfg)
+    pairs = [(0, 0), (0, 13)]
+    out, lse = vo.verify_attention(x.q, x.k_cache, x.v_cache, x.k_draft, x.v_draft, x.parent, heads=pairs)
+    anc = vo.ancestor_mask(x.parent[0])
+    for n, (b, h) in enumerate(pairs):
+        kv = h // cfg.G
+        f = lambda a: torch.from_numpy(vo.bf16_bits_to_f64(a)).float()
+        k = torch.cat([f(x.k_cache[b, kv]), f(x.k_draft[b, kv])])
+        v = torch.cat([f(x.v_cache[b, kv]), f(x.v_draft[b, kv])])
+        mask = torch.cat([torch.ones(cfg.N, cfg.L, dtype=torch.bool), torch.from_numpy(anc)], 1)
+        ref = torch.nn.functional.scaled_dot_product_attention(f(x.q[b, h])[None], k[None], v[None],
+                                                              attn_mask=mask[None])[0]
+        np.testing.assert_allclose(out[n], ref.double().numpy(), rtol=1e-4, atol=1e-5)
+
+
+# ---------------------------------------------------------------------------
+# input conversion
+
+
+def test_bf16_bits_and_rounding():
+    bits = np.array([0x3F80, 0xC000, 0x7F80, 0x0000, 0x8000, 0x3FC0], dtype=np.uint16)
+    np.testing.assert_array_equal(vo.bf16_bits_to_f64(bits), [1.0, -2.0, np.inf, 0.0, -0.0, 1.5])
+    x = np.array([1 + 2 ** -8, 1 + 3 * 2 ** -8, 1 + 2 ** -8 + 2 ** -20, -1.0, 3.0], dtype=np.float32)
+    np.testing.assert_array_equal(synth.f32_to_bf16_bits(x),
+                                  np.array([0x3F80, 0x3F82, 0x3F81, 0xBF80, 0x4040], dtype=np.uint16))
+
+
+# ---------------------------------------------------------------------------
+# selector
+
+
+def _key(x):
+    """Total order of a score: NaN lowest, then the numbers (-0 == +0)."""
+    return (0, 0.0) if math.isnan(x) else (1, x + 0.0)
+
+
+def _top_by_count(score, cand, r):
+    """j is in the top r of cand iff fewer than r members beat it (higher, or equal and lower index)."""
+    out = []
+    for j in cand:
+        beat = sum(1 for k in cand if _key(score[k]) > _key(score[j]) or
+                   (_key(score[k]) == _key(score[j]) and k < j))
+        if beat < r:
+            out.append(j)
+    return out
+
+
+def brute_select(draft, target, sink, window, m, budget):
+    L = len(draft)
+    if budget >= L:
+        return list(range(L))
+    prot = [j for j in range(L) if j < sink or j >= L - window]
+    free = [j for j in range(L) if j not in prot]
+    rest = budget - len(prot)
+    m1 = min(m, rest, len(free))
+    dsel = _top_by_count(draft, free, m1)
+    remaining = [j for j in free if j not in dsel]
+    tsel = _top_by_count(target, remaining, rest - m1)
+    return sorted(prot + dsel + tsel)
+
+
+def test_selector_hand_example():
+    g = json.load(open(os.path.join(GOLDEN, "select_hand_example.json")))
+    idx = vo.select_verify_set(np.array([g["draft_score"]], np.float32), np.array([g["target_score"]], np.float32),
+                               g["sink"], g["window"], g["top_m"], g["budget"])
+    assert idx[0].tolist() == g["expected_idx"]
+
+
+def test_selector_exhaustive_small_with_ties():
+    rng = np.random.default_rng(50)
+    levels = np.array([-1.0, 0.0, 2.5], dtype=np.float32)
+    n_cases = 0
+    for L in range(1, 11):
+        for _ in range(6):
+            d = levels[rng.integers(0, 3, L)]
+            t = levels[rng.integers(0, 3, L)]
+            for sink, window in itertools.product(range(0, 3), range(0, 3)):
+                p = len(vo.protected_set(L, sink, window))
+                for budget in range(p, L + 2):
+                    for m in range(0, budget - p + 2):
+                        got = vo.select_row(d, t, sink, window, m, budget).tolist()
+                        assert got == brute_select(d.tolist(), t.tolist(), sink, window, m, budget)
+                        n_cases += 1
+    assert n_cases > 3000
+
+
+def test_selector_special_values_order():
+    d = np.array([np.nan, -np.inf, -0.0, 0.0, np.inf, -1.0, np.nan, 1e-30], dtype=np.float32)
+    t = np.zeros(8, dtype=np.float32)
+    for r in range(0, 9):
+        got = vo.select_row(d, t, 0, 0, r, r).tolist()
+        assert got == brute_select(d.tolist(), t.tolist(), 0, 0, r, r)
+    # explicit: +inf, 1e-30, then -0 and +0 tie (lower index 2 first), -1, -inf, NaN(1), NaN(6)
+    assert vo.select_row(d, t, 0, 0, 3, 3).tolist() == [2, 4, 7]
+    assert vo.select_row(d, t, 0, 0, 7, 7).tolist() == [0, 1, 2, 3, 4, 5, 7]
+
+
+@settings(max_examples=150, deadline=None)
+@given(st.integers(1, 40), st.integers(0, 6), st.integers(0, 6), st.integers(0, 50), st.integers(0, 50),
+       st.integers(0, 2 ** 31 - 1))
+def test_selector_random_vs_brute(L, sink, window, m, extra, seed):
+    rng = np.random.default_rng(seed)
+    d = rng.integers(-3, 4, L).astype(np.float32)
+    t = rng.lognormal(0, 2, L).astype(np.float32)
+    p = len(vo.protected_set(L, sink, window))
+    budget = p + extra % (L + 2)
+    got = vo.select_row(d, t, sink, window, m, budget).tolist()
+    assert got == brute_select(d.tolist(), t.tolist(), sink, window, m, budget)
+
+
+def test_selector_special_cases():
+    rng = np.random.default_rng(51)
+    B, L = 3, 200
+    d = rng.lognormal(0, 2, (B, L)).astype(np.float32)
+    t = rng.lognormal(0, 2, (B, L)).astype(np.float32)
+    S, W = 4, 16
+    # budget >= L: everything
+    assert (vo.select_verify_set(d, t, S, W, 10, L) == np.arange(L)).all()
+    assert (vo.select_verify_set(d, t, S, W, 10, L + 5) == np.arange(L)).all()
+    # budget == sink + window: the StreamingLLM set
+    sw = vo.select_verify_set(d, t, S, W, 10, S + W)
+    assert (sw == np.r_[np.arange(S), np.arange(L - W, L)]).all()
+    # m == 0: pure target top-k; m == remaining budget: draft only
+    budget = 60
+    free = np.arange(S, L - W)
+    only_t = vo.select_verify_set(d, t, S, W, 0, budget)
+    only_d = vo.select_verify_set(d, t, S, W, budget - S - W, budget)
+    for b in range(B):
+        tk = free[np.argsort(-t[b, free], kind="stable")[:budget - S - W]]
+        dk = free[np.argsort(-d[b, free], kind="stable")[:budget - S - W]]
+        assert only_t[b].tolist() == sorted(np.r_[np.arange(S), tk, np.arange(L - W, L)].tolist())
+        assert only_d[b].tolist() == sorted(np.r_[np.arange(S), dk, np.arange(L - W, L)].tolist())
+    # invariants
+    idx = vo.select_verify_set(d, t, S, W, 20, budget)
+    for b in range(B):
+        assert len(idx[b]) == budget and (np.diff(idx[b]) > 0).all()
+        assert set(range(S)) | set(range(L - W, L)) <= set(idx[b].tolist())
+
+
+def test_selector_rejects_small_budget():
+    with pytest.raises(ValueError):
+        vo.select_row(np.zeros(50, np.float32), np.zeros(50, np.float32), 4, 16, 0, 10)
+
+
+def test_selector_config4_budget_split():
+    cfg = synth.small_variant(synth.CONFIGS["qwen25_7b_sparse2048_L32k"], L=4096, B=2)
+    x = synth.make_inputs(cfg)
+    idx = vo.select_verify_set(x.draft_score, x.target_score, cfg.sink, cfg.window, cfg.top_m, cfg.budget)
+    assert idx.shape == (2, cfg.budget)
