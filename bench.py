@@ -1,0 +1,218 @@
+"""Benchmark of speculative-verification attention on one MI355X.
+
+One step = one verification pass of one target-model layer over the whole
+batch, through the C ABI: the partial kernel (context splits + tree part) and
+the log-sum-exp merge; for a sparse workload the step also runs the verify-set
+selector.  Inputs are seeded synthetic tensors of the workload's shape
+(long_context_verify_tree_amd.synth), resident in HBM before timing starts;
+several copies are rotated so no step can reuse the previous step's data from
+the 256 MB MALL.
+
+Prints one JSON line.  `value` is the algorithmic HBM throughput of the whole
+step in GB/s (bytes the method must move / step time); the same line carries
+draft tokens verified per second per layer, the roofline fraction of the
+dominant kernel (timed with HIP events on the stream it runs on) and the CPU
+oracle timed on a bounded sample of the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0 # dense bf16
+MFMA_FP32_PEAK_TFLOPS = 157.3
+DEFAULT_CONFIG = "llama3_8b_chain8_L32k"
+
+
+def algorithmic(cfg, n_ctx: int, sparse: bool):
+    """Bytes and flops the method must move / compute for one step."""
+    e = 4 if cfg.dtype == "fp32" else 2
+    B, Hq, Hkv, D, N = cfg.B, cfg.Hq, cfg.Hkv, cfg.D, cfg.N
+    kv = 2 * B * Hkv * n_ctx * D * e
+    q = B * Hq * N * D * e
+    draft = 2 * B * Hkv * N * D * e
+    out = B * Hq * N * D * e + B * Hq * N * 4
+    idx = B * n_ctx * 4 if sparse else 0
+    parent = B * N * 4
+    flops = 4 * B * Hq * N * n_ctx * D
+    return dict(kv=kv, partial_bytes=kv + q + draft + parent + idx, step_bytes=kv + q + draft + out + idx + parent,
+                flops=flops)
+
+
+def cpu_baseline(cfg, x, budget_s: float):
+    """The oracle, untouched, on as many (sequence, KV-head group) slabs of the
+    benchmarked inputs as fit the time budget."""
+    from threadpoolctl import threadpool_info
+    from oracle import verify_oracle as vo
+
+    sparse = cfg.sparse and not cfg.dense
+    t0 = time.perf_counter()
+    idx = None
+    if sparse:
+        idx = vo.select_verify_set(x.draft_score, x.target_score, cfg.sink, cfg.window, cfg.top_m, cfg.budget)
+    groups = [(b, kvh) for b in range(cfg.B) for kvh in range(cfg.Hkv)]
+    done = 0
+    while done < len(groups) and time.perf_counter() - t0 < budget_s:
+        b, kvh = groups[done]
+        vo.verify_attention(x.q, x.k_cache, x.v_cache, x.k_draft, x.v_draft, x.parent, ctx_index=idx,
+                            heads=[(b, kvh * cfg.G + g) for g in range(cfg.G)])
+        done += 1
+    dt = time.perf_counter() - t0
+    n_ctx = min(cfg.budget, cfg.L) if sparse else cfg.L
+    frac = done / len(groups)
+    sample_bytes = algorithmic(cfg, n_ctx, sparse)["step_bytes"] * frac
+    threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    return {
+        "value": round(sample_bytes / dt / 1e9, 4),
+        "unit": "GB/s",
+        "tokens_per_s_per_layer": round(cfg.B * cfg.N * frac / dt, 3),
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"{done}/{len(groups)} (sequence, KV head) slabs of the benchmarked {cfg.name} inputs"
+                  f"{' incl. selection' if sparse else ''}, fp64 numpy, {dt:.1f} s",
+        "host_cpus": os.cpu_count(),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default=DEFAULT_CONFIG)
+    ap.add_argument("--copies", type=int, default=0, help="input copies rotated over steps (0: auto)")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}); the kernels use no collectives",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from long_context_verify_tree_amd import ops, synth
+
+    ops.load()
+    cfg = synth.CONFIGS[args.config]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    sparse = cfg.sparse and not cfg.dense
+    print(f"[bench] generating {cfg.name}", file=sys.stderr, flush=True)
+    x = synth.make_inputs(cfg, scores=cfg.sparse)
+
+    def dv(a, dt):
+        if dt == synth.BF16:
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    base = dict(q=dv(x.q, cfg.dtype), k_cache=dv(x.k_cache, cfg.dtype), v_cache=dv(x.v_cache, cfg.dtype),
+                k_draft=dv(x.k_draft, cfg.dtype), v_draft=dv(x.v_draft, cfg.dtype),
+                parent=torch.from_numpy(x.parent).to(dev))
+    if sparse:
+        base["draft_score"] = dv(x.draft_score, synth.FP32)
+        base["target_score"] = dv(x.target_score, synth.FP32)
+    a_bytes_kv = 2 * cfg.B * cfg.Hkv * cfg.L * cfg.D * (4 if cfg.dtype == "fp32" else 2)
+    copies = args.copies or max(2, min(8, int(np.ceil(1.2e9 / max(a_bytes_kv, 1)))))
+    sets = [base] + [{k: v.clone() for k, v in base.items()} for _ in range(copies - 1)]
+
+    n_ctx = min(cfg.budget, cfg.L) if sparse else cfg.L
+    out = torch.empty_like(base["q"])
+    lse = torch.empty(cfg.B, cfg.Hq, cfg.N, dtype=torch.float32, device=dev)
+    desc = ops.make_desc(base["q"], base["k_cache"], base["v_cache"], base["k_draft"], base["v_draft"], out)
+    ws = torch.empty(ops.workspace_size(desc, n_ctx), dtype=torch.uint8, device=dev)
+    idx_bufs = [torch.empty(cfg.B, n_ctx, dtype=torch.int32, device=dev) for _ in sets] if sparse else None
+
+    def step(i, ev=None):
+        s = sets[i % len(sets)]
+        if ev is not None:
+            ev[0].record()
+        idx = None
+        if sparse:
+            idx = ops.select_verify_set(s["draft_score"], s["target_score"], sink=cfg.sink, window=cfg.window,
+                                        top_m=cfg.top_m, budget=cfg.budget, out=idx_bufs[i % len(sets)])
+        if ev is not None:
+            ev[1].record()
+        ops.verify_attn_partials(desc, s["q"], s["k_cache"], s["v_cache"], s["k_draft"], s["v_draft"],
+                                 s["parent"], ws, verify_idx=idx)
+        if ev is not None:
+            ev[2].record()
+        ops.verify_attn_merge(desc, n_ctx, out, lse, ws)
+        if ev is not None:
+            ev[3].record()
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i, evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    sel_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    part_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    merge_ms = [e[2].elapsed_time(e[3]) for e in evs]
+    ms_per_step = wall * 1e3 / args.steps
+    a = algorithmic(cfg, n_ctx, sparse)
+    value = a["step_bytes"] / (ms_per_step * 1e-3) / 1e9
+    part_avg = statistics.mean(part_ms)
+    achieved = a["partial_bytes"] / (part_avg * 1e-3) / 1e9
+    flops_rate = a["flops"] / (part_avg * 1e-3) / 1e12
+    mfma_bound = a["flops"] / a["partial_bytes"] > (MFMA_BF16_PEAK_TFLOPS * 1e12) / (HBM_PEAK_GBS * 1e9)
+    if mfma_bound:
+        roof = {"bound": "mfma", "achieved": round(flops_rate, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(flops_rate / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None}
+    else:
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None}
+    roof["kernel"] = "partial_kernel"
+    roof["kernel_avg_us"] = round(part_avg * 1e3, 2)
+    roof["algorithmic_bytes_per_launch"] = a["partial_bytes"]
+    roof["algorithmic_flops_per_launch"] = a["flops"]
+
+    line = {
+        "metric": "verify-attention HBM GB/s (% of peak) + draft tokens verified/sec per layer",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "draft_tokens_verified_per_s_per_layer": round(cfg.B * cfg.N / (ms_per_step * 1e-3), 1),
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "stage_ms": {"select": round(statistics.median(sel_ms), 4), "partials": round(statistics.median(part_ms), 4),
+                     "merge": round(statistics.median(merge_ms), 4)},
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": f"synthetic (seeded N(0,1) q/K/V, {cfg.tree} tree; {copies} rotated input copies)",
+        "config": {"workload": cfg.name, "batch": cfg.B, "q_heads": cfg.Hq, "kv_heads": cfg.Hkv,
+                   "head_dim": cfg.D, "context": cfg.L, "draft_nodes": cfg.N, "tree": cfg.tree,
+                   "verify": "sparse" if sparse else "dense", "n_ctx_keys": n_ctx},
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle sample", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(cfg, x, args.cpu_budget)
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,183 @@
+/*
+ * verify_attn.h -- speculative-verification attention for AMD MI355X (gfx950).
+ *
+ * C ABI of libverify_attn.so.  Plain pointers and sizes only.
+ *
+ * What is computed
+ * ----------------
+ * A target model verifies N draft tokens in one forward pass.  The drafts
+ * form a prefix tree given as a parent array (BASTION, "Drafting a
+ * Diffusione a Blocchi Basato su Albero": marginal candidates combined into
+ * a prefix tree; a chain is the special case of a single draft block, as in
+ * the Dustin summary, "Workflow di Verifica").  For every sequence b, query
+ * head h (reading KV head h / (Hq / Hkv)) and draft node i, the output row is
+ *
+ *     out[b,h,i,:] = sum_j softmax(s)_j * value_j,    s_j = scale * <q[b,h,i,:], key_j>
+ *     lse[b,h,i]   = ln sum_j exp(s_j)
+ *
+ * over the key set  C_b  U  anc(i), where
+ *   - C_b is the context part: every cached token [0, L) (dense), or the
+ *     verify set I_verify = {verify_idx[b, 0..K)} read in place from the
+ *     full cache (sparse; Dustin, "Workflow di Verifica" steps 3-4 and
+ *     "Significato e Limitazioni": the cache is indexed, not evicted);
+ *   - anc(i) is node i and its ancestors among the draft tokens: the tree
+ *     mask of the speculative part (LongSpec, "Tree Attention Ibrida").
+ * The context part has no mask.  The library computes it as split partial
+ * results plus one tree-masked partial and joins them with a log-sum-exp
+ * merge, which is exact (LongSpec, "Tree Attention Ibrida", aggregation).
+ *
+ * select_verify_set builds I_verify per sequence (Dustin, "Aggregazione
+ * Ibrida dell'Attenzione"): the attention-sink prefix [0, sink) and the local
+ * window [L - window, L) are kept; the remaining budget is filled first by
+ * the top min(top_m, remaining) tokens by draft-lookahead score, then by the
+ * best remaining tokens by target-historical score.  Ties go to the lower
+ * token index; NaN ranks below -inf; -0 equals +0.  Output is ascending.
+ *
+ * Conventions (all entry points)
+ * ------------------------------
+ * - Every tensor pointer is a DEVICE pointer owned by the caller.  The
+ *   library never allocates, frees or keeps a pointer past the call.
+ * - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL is the
+ *   default stream); no call synchronises.  Buffers must stay alive until the
+ *   stream has finished the work.
+ * - Argument errors are detected on the host before anything is enqueued and
+ *   reported as VA_EINVAL / VA_EUNSUPPORTED / VA_EWORKSPACE; nothing runs.
+ *   VA_EHIP reports a failed kernel launch; kernels of that call that were
+ *   already enqueued may have run.  va_last_error() gives a message for the
+ *   last failing call on the calling thread.
+ * - Device-side preconditions (parent, verify_idx contents) are not checked
+ *   synchronously.  Violations stay memory-safe: a parent outside [-1, i) is
+ *   treated as -1 and an index outside [0, L) is skipped, with an unspecified
+ *   (but finite) result.
+ * - Workspace contents need no initialisation and are not preserved.
+ *   Concurrent calls must use distinct workspaces.
+ * - Calls keep no global mutable state and are thread-safe.
+ */
+#ifndef VERIFY_ATTN_H
+#define VERIFY_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum va_status {
+  VA_OK = 0,
+  VA_EINVAL = 1,        /* malformed argument (null pointer, bad size, bad stride) */
+  VA_EUNSUPPORTED = 2,  /* well-formed but outside what the kernels implement     */
+  VA_EWORKSPACE = 3,    /* workspace missing or smaller than required             */
+  VA_EHIP = 4           /* a HIP launch failed                                     */
+} va_status;
+
+typedef enum va_dtype {
+  VA_FP32 = 0,          /* float32 inputs and output, float32 arithmetic           */
+  VA_BF16 = 1           /* bfloat16 inputs and output, float32 accumulation        */
+} va_dtype;
+
+/* Shape and layout of one verification problem (one target-model layer).
+ *
+ *   q        [B, Hq,  N, D]   queries of the draft nodes (after RoPE)
+ *   k_cache  [B, Hkv, L, D]   committed context keys     (v_cache alike)
+ *   k_draft  [B, Hkv, N, D]   draft-node keys            (v_draft alike)
+ *   out      [B, Hq,  N, D]
+ *
+ * Each tensor is addressed with element strides over its three outer axes
+ * (batch, head, row); the innermost (D) stride is 1.  Token-major caches
+ * ([B, L, Hkv, D]) are expressed through the strides.  Base pointers and all
+ * strides must keep every row 16-byte aligned. */
+typedef struct va_attn_desc {
+  int32_t B;            /* sequences, >= 1                                     */
+  int32_t Hq;           /* query heads, >= 1, multiple of Hkv                  */
+  int32_t Hkv;          /* key/value heads, >= 1                               */
+  int32_t D;            /* head dimension: 64 or 128                           */
+  int32_t L;            /* committed context length, >= 0 (0: tree part only)  */
+  int32_t N;            /* draft nodes per sequence, 1..256                    */
+  int32_t dtype;        /* va_dtype of q, caches, drafts and out               */
+  float scale;          /* softmax scale; <= 0 selects 1/sqrt(D)               */
+  int64_t q_stride[3];  /* q over (b, query head, node)                        */
+  int64_t kc_stride[3]; /* k_cache over (b, kv head, token)                    */
+  int64_t vc_stride[3]; /* v_cache over (b, kv head, token)                    */
+  int64_t kd_stride[3]; /* k_draft over (b, kv head, node)                     */
+  int64_t vd_stride[3]; /* v_draft over (b, kv head, node)                     */
+  int64_t o_stride[3];  /* out over (b, query head, node)                      */
+} va_attn_desc;
+
+/* Workspace bytes needed by verify_attn_dense (n_ctx = L) or
+ * verify_attn_sparse (n_ctx = K).  *bytes is set on VA_OK. */
+va_status va_attn_workspace_size(const va_attn_desc* desc, int32_t n_ctx, size_t* bytes);
+
+/* Dense verification: context part over every cached token [0, L).
+ *   parent  [B, N] int32, contiguous; parent[b,i] in [-1, i) (-1: the node
+ *           follows the last committed token, which is part of the context)
+ *   out     [B, Hq, N, D] in desc->dtype (strides desc->o_stride)
+ *   lse     [B, Hq, N] float32 contiguous, natural log; may be NULL
+ *   ws      device workspace of at least va_attn_workspace_size(desc, L) bytes */
+va_status verify_attn_dense(const va_attn_desc* desc,
+                            const void* q, const void* k_cache, const void* v_cache,
+                            const void* k_draft, const void* v_draft,
+                            const int32_t* parent,
+                            void* out, float* lse,
+                            void* ws, size_t ws_bytes, void* stream);
+
+/* Sparse verification: context part over the verify set only.
+ *   verify_idx  [B, K] int32, row stride idx_stride (>= K); each row holds K
+ *               distinct token positions in [0, L) (any order; ascending is
+ *               fastest).  0 <= K <= L.
+ * Other arguments as for verify_attn_dense; ws needs
+ * va_attn_workspace_size(desc, K) bytes. */
+va_status verify_attn_sparse(const va_attn_desc* desc,
+                             const void* q, const void* k_cache, const void* v_cache,
+                             const void* k_draft, const void* v_draft,
+                             const int32_t* parent,
+                             const int32_t* verify_idx, int32_t K, int64_t idx_stride,
+                             void* out, float* lse,
+                             void* ws, size_t ws_bytes, void* stream);
+
+/* The two stages that verify_attn_dense / verify_attn_sparse enqueue, for
+ * callers that time or schedule them separately.  verify_attn_partials
+ * writes the split context partials and the tree partial into ws
+ * (verify_idx == NULL: dense over [0, L) and K is ignored; otherwise sparse
+ * over the K indices); verify_attn_merge joins them into out / lse.  The
+ * merge must be given the same desc and ws and n_ctx = L (dense) or K
+ * (sparse), and must run after the partials on the stream. */
+va_status verify_attn_partials(const va_attn_desc* desc,
+                               const void* q, const void* k_cache, const void* v_cache,
+                               const void* k_draft, const void* v_draft,
+                               const int32_t* parent,
+                               const int32_t* verify_idx, int32_t K, int64_t idx_stride,
+                               void* ws, size_t ws_bytes, void* stream);
+va_status verify_attn_merge(const va_attn_desc* desc, int32_t n_ctx,
+                            void* out, float* lse,
+                            const void* ws, size_t ws_bytes, void* stream);
+
+/* Workspace bytes needed by select_verify_set for B rows of L scores. */
+va_status va_select_workspace_size(int32_t B, int32_t L, size_t* bytes);
+
+/* Verify-set selection.
+ *   draft_score, target_score  [B, L] float32, row stride ld (>= L)
+ *   sink, window, top_m >= 0; budget >= min(L, |[0,sink) U [L-window,L)|)
+ *   verify_idx  [B, min(budget, L)] int32, contiguous; ascending, distinct
+ *   ws          device workspace of va_select_workspace_size(B, L) bytes
+ * budget >= L returns every index 0..L-1. */
+va_status select_verify_set(const float* draft_score, const float* target_score,
+                            int32_t B, int32_t L, int64_t ld,
+                            int32_t sink, int32_t window, int32_t top_m, int32_t budget,
+                            int32_t* verify_idx,
+                            void* ws, size_t ws_bytes, void* stream);
+
+/* Static description of a status code. */
+const char* va_status_str(va_status status);
+
+/* Message describing the last failing call on this thread ("" if none). */
+const char* va_last_error(void);
+
+/* Library version, as MAJOR * 10000 + MINOR * 100 + PATCH. */
+int32_t va_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VERIFY_ATTN_H */

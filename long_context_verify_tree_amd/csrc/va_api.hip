@@ -1,0 +1,277 @@
+// Host side of libverify_attn.so: argument validation, work planning and
+// kernel launches behind the C ABI of include/verify_attn.h.
+//
+// Every check runs on the host before the first HIP call, so a rejected call
+// enqueues nothing.  The library keeps no state between calls.
+
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <hip/hip_runtime.h>
+
+#include "../../include/verify_attn.h"
+#include "va_internal.h"
+#include "va_select.h"
+
+namespace {
+
+thread_local char g_msg[512] = "";
+
+va_status fail(va_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_msg, sizeof(g_msg), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+va_status ok() {
+  g_msg[0] = '\0';
+  return VA_OK;
+}
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+va_status check_desc(const va_attn_desc* d) {
+  if (d == nullptr) return fail(VA_EINVAL, "desc is NULL");
+  if (d->B < 1 || d->Hq < 1 || d->Hkv < 1) return fail(VA_EINVAL, "B, Hq, Hkv must be >= 1");
+  if (d->Hq % d->Hkv != 0) return fail(VA_EINVAL, "Hq (%d) must be a multiple of Hkv (%d)", d->Hq, d->Hkv);
+  if (d->L < 0) return fail(VA_EINVAL, "L must be >= 0");
+  if (d->N < 1) return fail(VA_EINVAL, "N must be >= 1");
+  if (d->N > 256) return fail(VA_EUNSUPPORTED, "N = %d exceeds 256 draft nodes", d->N);
+  if (d->D != 64 && d->D != 128) return fail(VA_EUNSUPPORTED, "D = %d (supported: 64, 128)", d->D);
+  if (d->dtype != VA_FP32 && d->dtype != VA_BF16) return fail(VA_EINVAL, "unknown dtype %d", d->dtype);
+  if (isnan(d->scale) || isinf(d->scale)) return fail(VA_EINVAL, "scale must be finite");
+  const int64_t vec = d->dtype == VA_BF16 ? 8 : 4;  // elements per 16 bytes
+  const int64_t* strides[6] = {d->q_stride, d->kc_stride, d->vc_stride, d->kd_stride, d->vd_stride, d->o_stride};
+  const char* names[6] = {"q", "k_cache", "v_cache", "k_draft", "v_draft", "out"};
+  for (int t = 0; t < 6; ++t)
+    for (int a = 0; a < 3; ++a)
+      if (strides[t][a] % vec != 0)
+        return fail(VA_EINVAL, "%s stride[%d] = %lld breaks 16-byte row alignment", names[t], a,
+                    (long long)strides[t][a]);
+  return VA_OK;
+}
+
+bool misaligned(const void* p) { return ((uintptr_t)p & 15u) != 0; }
+
+va::Plan make_plan(const va_attn_desc* d, int32_t n_ctx) {
+  va::Plan pl{};
+  const int G = d->Hq / d->Hkv;
+  const int R = G * d->N;
+  pl.rb = R <= 32 ? 1 : 2;
+  const int rows_per_tile = 32 * pl.rb;
+  pl.row_tiles = (R + rows_per_tile - 1) / rows_per_tile;
+  const int64_t pairs = (int64_t)d->B * d->Hkv * pl.row_tiles;
+  // Enough context workgroups to cover the chip a few times over, but no
+  // split shorter than 512 keys: every split costs one partial row per query
+  // row in the workspace.
+  const int64_t target_groups = 1024;
+  int64_t want_splits = (target_groups + pairs - 1) / pairs;
+  if (want_splits < 1) want_splits = 1;
+  int64_t len = n_ctx > 0 ? (n_ctx + want_splits - 1) / want_splits : 128;
+  len = (len + 127) / 128 * 128;
+  if (len < 512) len = 512;
+  pl.split_len = (int)len;
+  pl.n_ctx_splits = n_ctx > 0 ? (int)((n_ctx + len - 1) / len) : 0;
+  pl.n_parts = pl.n_ctx_splits + 1;
+  pl.rows = (int64_t)d->B * d->Hq * d->N;
+  const size_t o_bytes = (size_t)pl.rows * pl.n_parts * d->D * sizeof(float);
+  pl.off_lse = align_up(o_bytes);
+  pl.ws_bytes = pl.off_lse + align_up((size_t)pl.rows * pl.n_parts * sizeof(float));
+  return pl;
+}
+
+float eff_scale(const va_attn_desc* d) { return d->scale > 0.f ? d->scale : 1.0f / sqrtf((float)d->D); }
+
+va_status run_partials(const va_attn_desc* d, const void* q, const void* kc, const void* vc, const void* kd,
+                       const void* vd, const int32_t* parent, bool sparse, const int32_t* idx, int32_t K,
+                       int64_t idx_stride, void* ws, size_t ws_bytes, hipStream_t stream) {
+  va_status st = check_desc(d);
+  if (st != VA_OK) return st;
+  const int32_t n_ctx = sparse ? K : d->L;
+  if (sparse) {
+    if (K < 0 || K > d->L) return fail(VA_EINVAL, "K = %d outside [0, L = %d]", K, d->L);
+    if (K > 0 && idx == nullptr) return fail(VA_EINVAL, "verify_idx must be non-NULL when K > 0");
+    if (K > 0 && idx_stride < K) return fail(VA_EINVAL, "idx_stride (%lld) < K (%d)", (long long)idx_stride, K);
+  }
+  if (!q || !kd || !vd || !parent) return fail(VA_EINVAL, "q, k_draft, v_draft and parent must be non-NULL");
+  if (n_ctx > 0 && (!kc || !vc)) return fail(VA_EINVAL, "k_cache and v_cache must be non-NULL when L > 0");
+  if (misaligned(q) || misaligned(kc) || misaligned(vc) || misaligned(kd) || misaligned(vd))
+    return fail(VA_EINVAL, "tensor base pointers must be 16-byte aligned");
+  const va::Plan pl = make_plan(d, n_ctx);
+  if (ws_bytes < pl.ws_bytes || ws == nullptr)
+    return fail(VA_EWORKSPACE, "workspace of %zu bytes needed, %zu given", pl.ws_bytes, ws ? ws_bytes : (size_t)0);
+  const int64_t groups = (int64_t)d->B * d->Hkv * pl.row_tiles * pl.n_parts;
+  if (groups > 0x7fffffff) return fail(VA_EUNSUPPORTED, "problem too large for one launch");
+  const bool gather = sparse && n_ctx > 0;
+
+  va::PartialParams p{};
+  p.q = q;
+  p.kc = kc;
+  p.vc = vc;
+  p.kd = kd;
+  p.vd = vd;
+  p.parent = parent;
+  p.idx = gather ? idx : nullptr;
+  p.idx_stride = gather ? idx_stride : 0;
+  for (int a = 0; a < 3; ++a) {
+    p.qs[a] = d->q_stride[a];
+    p.kcs[a] = d->kc_stride[a];
+    p.vcs[a] = d->vc_stride[a];
+    p.kds[a] = d->kd_stride[a];
+    p.vds[a] = d->vd_stride[a];
+  }
+  p.part_o = (float*)ws;
+  p.part_lse = (float*)((char*)ws + pl.off_lse);
+  p.B = d->B;
+  p.Hq = d->Hq;
+  p.Hkv = d->Hkv;
+  p.G = d->Hq / d->Hkv;
+  p.N = d->N;
+  p.L = d->L;
+  p.n_ctx = n_ctx;
+  p.R = p.G * d->N;
+  p.row_tiles = pl.row_tiles;
+  p.split_len = pl.split_len;
+  p.n_ctx_splits = pl.n_ctx_splits;
+  p.n_parts = pl.n_parts;
+  p.total_groups = (int)groups;
+  p.c = eff_scale(d) * 1.4426950408889634f;
+  hipError_t e = va::launch_partials(p, d->dtype, d->D, pl.rb, gather, stream);
+  if (e != hipSuccess) return fail(VA_EHIP, "partial kernel launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+va_status run_merge(const va_attn_desc* d, int32_t n_ctx, void* out, float* lse, const void* ws, size_t ws_bytes,
+                    hipStream_t stream) {
+  va_status st = check_desc(d);
+  if (st != VA_OK) return st;
+  if (n_ctx < 0 || n_ctx > d->L) return fail(VA_EINVAL, "n_ctx = %d outside [0, L]", n_ctx);
+  if (!out) return fail(VA_EINVAL, "out must be non-NULL");
+  if (misaligned(out)) return fail(VA_EINVAL, "out must be 16-byte aligned");
+  const va::Plan pl = make_plan(d, n_ctx);
+  if (ws_bytes < pl.ws_bytes || ws == nullptr)
+    return fail(VA_EWORKSPACE, "workspace of %zu bytes needed, %zu given", pl.ws_bytes, ws ? ws_bytes : (size_t)0);
+  va::MergeParams m{};
+  m.part_o = (const float*)ws;
+  m.part_lse = (const float*)((const char*)ws + pl.off_lse);
+  m.out = out;
+  m.lse = lse;
+  for (int a = 0; a < 3; ++a) m.os[a] = d->o_stride[a];
+  m.rows = pl.rows;
+  m.Hq = d->Hq;
+  m.N = d->N;
+  m.n_parts = pl.n_parts;
+  hipError_t e = va::launch_merge(m, d->dtype, d->D, stream);
+  if (e != hipSuccess) return fail(VA_EHIP, "merge kernel launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+va_status va_attn_workspace_size(const va_attn_desc* desc, int32_t n_ctx, size_t* bytes) {
+  va_status st = check_desc(desc);
+  if (st != VA_OK) return st;
+  if (bytes == nullptr) return fail(VA_EINVAL, "bytes is NULL");
+  if (n_ctx < 0 || n_ctx > desc->L) return fail(VA_EINVAL, "n_ctx = %d outside [0, L]", n_ctx);
+  *bytes = make_plan(desc, n_ctx).ws_bytes;
+  return ok();
+}
+
+va_status verify_attn_partials(const va_attn_desc* desc, const void* q, const void* k_cache, const void* v_cache,
+                               const void* k_draft, const void* v_draft, const int32_t* parent,
+                               const int32_t* verify_idx, int32_t K, int64_t idx_stride, void* ws,
+                               size_t ws_bytes, void* stream) {
+  return run_partials(desc, q, k_cache, v_cache, k_draft, v_draft, parent, verify_idx != nullptr, verify_idx, K,
+                      idx_stride, ws, ws_bytes, (hipStream_t)stream);
+}
+
+va_status verify_attn_merge(const va_attn_desc* desc, int32_t n_ctx, void* out, float* lse, const void* ws,
+                            size_t ws_bytes, void* stream) {
+  return run_merge(desc, n_ctx, out, lse, ws, ws_bytes, (hipStream_t)stream);
+}
+
+va_status verify_attn_dense(const va_attn_desc* desc, const void* q, const void* k_cache, const void* v_cache,
+                            const void* k_draft, const void* v_draft, const int32_t* parent, void* out,
+                            float* lse, void* ws, size_t ws_bytes, void* stream) {
+  va_status st = check_desc(desc);
+  if (st != VA_OK) return st;
+  if (!out) return fail(VA_EINVAL, "out must be non-NULL");
+  if (misaligned(out)) return fail(VA_EINVAL, "out must be 16-byte aligned");
+  st = run_partials(desc, q, k_cache, v_cache, k_draft, v_draft, parent, false, nullptr, desc->L, 0, ws, ws_bytes,
+                    (hipStream_t)stream);
+  if (st != VA_OK) return st;
+  return run_merge(desc, desc->L, out, lse, ws, ws_bytes, (hipStream_t)stream);
+}
+
+va_status verify_attn_sparse(const va_attn_desc* desc, const void* q, const void* k_cache, const void* v_cache,
+                             const void* k_draft, const void* v_draft, const int32_t* parent,
+                             const int32_t* verify_idx, int32_t K, int64_t idx_stride, void* out, float* lse,
+                             void* ws, size_t ws_bytes, void* stream) {
+  va_status st = check_desc(desc);
+  if (st != VA_OK) return st;
+  if (!out) return fail(VA_EINVAL, "out must be non-NULL");
+  if (misaligned(out)) return fail(VA_EINVAL, "out must be 16-byte aligned");
+  st = run_partials(desc, q, k_cache, v_cache, k_draft, v_draft, parent, true, verify_idx, K, idx_stride, ws,
+                    ws_bytes, (hipStream_t)stream);
+  if (st != VA_OK) return st;
+  return run_merge(desc, K, out, lse, ws, ws_bytes, (hipStream_t)stream);
+}
+
+va_status va_select_workspace_size(int32_t B, int32_t L, size_t* bytes) {
+  if (bytes == nullptr) return fail(VA_EINVAL, "bytes is NULL");
+  if (B < 0 || L < 0) return fail(VA_EINVAL, "B and L must be >= 0");
+  *bytes = va::select_ws_bytes(B, L);
+  return ok();
+}
+
+va_status select_verify_set(const float* draft_score, const float* target_score, int32_t B, int32_t L, int64_t ld,
+                            int32_t sink, int32_t window, int32_t top_m, int32_t budget, int32_t* verify_idx,
+                            void* ws, size_t ws_bytes, void* stream) {
+  if (B < 0 || L < 0) return fail(VA_EINVAL, "B and L must be >= 0");
+  if (sink < 0 || window < 0 || top_m < 0 || budget < 0)
+    return fail(VA_EINVAL, "sink, window, top_m and budget must be >= 0");
+  if (ld < L) return fail(VA_EINVAL, "ld (%lld) < L (%d)", (long long)ld, L);
+  const int64_t k_out = budget < L ? budget : L;
+  if (B == 0 || k_out == 0) return ok();
+  const int64_t sink_n = sink < L ? sink : L;
+  const int64_t win_lo = L - (int64_t)(window < L ? window : L);
+  const int64_t protected_n = (win_lo > sink_n ? sink_n + (L - win_lo) : L);
+  if (budget < L && budget < protected_n)
+    return fail(VA_EINVAL, "budget (%d) smaller than sink + window (%lld)", budget, (long long)protected_n);
+  if (!verify_idx) return fail(VA_EINVAL, "verify_idx must be non-NULL");
+  if (budget < L && L > va::kSelectMaxL)
+    return fail(VA_EUNSUPPORTED, "L = %d exceeds the selector limit of %d tokens", L, va::kSelectMaxL);
+  if (budget < L && (!draft_score || !target_score))
+    return fail(VA_EINVAL, "draft_score and target_score must be non-NULL");
+  const size_t need = va::select_ws_bytes(B, L);
+  if (need > 0 && (ws == nullptr || ws_bytes < need))
+    return fail(VA_EWORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws ? ws_bytes : (size_t)0);
+  hipError_t e = va::launch_select(draft_score, target_score, B, L, ld, sink, window, top_m, budget, verify_idx, ws,
+                                   (hipStream_t)stream);
+  if (e != hipSuccess) return fail(VA_EHIP, "select kernel launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+const char* va_status_str(va_status s) {
+  switch (s) {
+    case VA_OK: return "ok";
+    case VA_EINVAL: return "invalid argument";
+    case VA_EUNSUPPORTED: return "unsupported shape or type";
+    case VA_EWORKSPACE: return "workspace missing or too small";
+    case VA_EHIP: return "HIP launch failed";
+  }
+  return "unknown status";
+}
+
+const char* va_last_error(void) { return g_msg; }
+
+int32_t va_version(void) { return 100; }
+
+}  // extern "C"

@@ -1,0 +1,65 @@
+// Internal declarations shared by the host API and the kernels of
+// libverify_attn.so.  Not installed; the public interface is verify_attn.h.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime.h>
+
+namespace va {
+
+// How one verification call is cut into workgroups.
+//
+// Rows: the G * N query rows that share one KV head (G query heads of the
+// group times N draft nodes) are cut into row tiles of 32 * rb rows.
+// Keys: the n_ctx context keys are cut into n_ctx_splits splits of
+// split_len keys; the draft (tree) keys form one more part.  Every
+// (sequence, kv head, row tile, part) is one workgroup that writes one
+// normalised partial output and its log2-sum-exp.
+struct Plan {
+  int rb;            // 32-row blocks per wave (1 or 2)
+  int row_tiles;     // ceil(G * N / (32 * rb))
+  int split_len;     // context keys per split (multiple of 128)
+  int n_ctx_splits;  // ceil(n_ctx / split_len); 0 when n_ctx == 0
+  int n_parts;       // n_ctx_splits + 1 (the tree part is last)
+  int64_t rows;      // B * Hq * N output rows
+  size_t off_lse;    // byte offset of the partial lse array in the workspace
+  size_t ws_bytes;   // total workspace bytes
+};
+
+struct PartialParams {
+  const void* q;
+  const void* kc;
+  const void* vc;
+  const void* kd;
+  const void* vd;
+  const int32_t* parent;
+  const int32_t* idx;   // verify set (sparse) or nullptr (dense)
+  int64_t idx_stride;
+  int64_t qs[3], kcs[3], vcs[3], kds[3], vds[3];
+  float* part_o;        // [rows][n_parts][D]
+  float* part_lse;      // [rows][n_parts], log2 domain
+  int B, Hq, Hkv, G, N, L, n_ctx;
+  int R;                // G * N
+  int row_tiles, split_len, n_ctx_splits, n_parts;
+  int total_groups;     // grid size
+  float c;              // scale * log2(e)
+};
+
+struct MergeParams {
+  const float* part_o;
+  const float* part_lse;
+  void* out;
+  float* lse;           // may be nullptr
+  int64_t os[3];
+  int64_t rows;
+  int Hq, N, n_parts;
+};
+
+// Launchers (defined in va_attn.hip).  Return the hipError_t of the launch.
+hipError_t launch_partials(const PartialParams& p, int dtype, int D, int rb, bool gather,
+                           hipStream_t stream);
+hipError_t launch_merge(const MergeParams& p, int dtype, int D, hipStream_t stream);
+
+}  // namespace va

@@ -1,0 +1,21 @@
+// Internal declarations of the verify-set selector.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime.h>
+
+namespace va {
+
+// Longest score row the selector handles: its token bitmap lives in LDS
+// (L / 8 bytes, at most 128 KiB of the 160 KiB per CU).
+constexpr int32_t kSelectMaxL = 1 << 20;
+
+size_t select_ws_bytes(int32_t B, int32_t L);
+
+hipError_t launch_select(const float* draft_score, const float* target_score, int32_t B, int32_t L, int64_t ld,
+                         int32_t sink, int32_t window, int32_t top_m, int32_t budget, int32_t* verify_idx,
+                         void* ws, hipStream_t stream);
+
+}  // namespace va

@@ -1,0 +1,251 @@
+"""Thin Python binding over libverify_attn.so (argument marshalling only).
+
+Every step of the computation runs in the HIP kernels behind the C ABI of
+``include/verify_attn.h``; this module turns torch tensors into pointers,
+strides and the current HIP stream, allocates outputs and workspaces with
+torch, and raises ``VerifyAttnError`` on a non-zero status.  There is no
+fallback: if the library cannot be loaded, every call raises.
+
+Names follow the C ABI: ``verify_attn_dense``, ``verify_attn_sparse``,
+``select_verify_set`` (plus the two stages ``verify_attn_partials`` /
+``verify_attn_merge`` and the workspace-size queries).
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch  # noqa: F401  -- must be loaded first so the library binds to torch's HIP runtime
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libverify_attn.so")
+
+VA_OK, VA_EINVAL, VA_EUNSUPPORTED, VA_EWORKSPACE, VA_EHIP = range(5)
+VA_FP32, VA_BF16 = 0, 1
+
+
+class VerifyAttnError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"verify_attn status {status}: {message}")
+        self.status = status
+
+
+class AttnDesc(ctypes.Structure):
+    _fields_ = [
+        ("B", ctypes.c_int32), ("Hq", ctypes.c_int32), ("Hkv", ctypes.c_int32),
+        ("D", ctypes.c_int32), ("L", ctypes.c_int32), ("N", ctypes.c_int32),
+        ("dtype", ctypes.c_int32), ("scale", ctypes.c_float),
+        ("q_stride", ctypes.c_int64 * 3), ("kc_stride", ctypes.c_int64 * 3),
+        ("vc_stride", ctypes.c_int64 * 3), ("kd_stride", ctypes.c_int64 * 3),
+        ("vd_stride", ctypes.c_int64 * 3), ("o_stride", ctypes.c_int64 * 3),
+    ]
+
+
+_lib = None
+_P = ctypes.c_void_p
+_DESC_P = ctypes.POINTER(AttnDesc)
+
+
+def _declare(lib):
+    i32, i64, sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    sig = {
+        "va_attn_workspace_size": (i32, [_DESC_P, i32, ctypes.POINTER(sz)]),
+        "verify_attn_dense": (i32, [_DESC_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, sz, _P]),
+        "verify_attn_sparse": (i32, [_DESC_P, _P, _P, _P, _P, _P, _P, _P, i32, i64, _P, _P, _P, sz, _P]),
+        "verify_attn_partials": (i32, [_DESC_P, _P, _P, _P, _P, _P, _P, _P, i32, i64, _P, sz, _P]),
+        "verify_attn_merge": (i32, [_DESC_P, i32, _P, _P, _P, sz, _P]),
+        "va_select_workspace_size": (i32, [i32, i32, ctypes.POINTER(sz)]),
+        "select_verify_set": (i32, [_P, _P, i32, i32, i64, i32, i32, i32, i32, _P, _P, sz, _P]),
+        "va_status_str": (ctypes.c_char_p, [i32]),
+        "va_last_error": (ctypes.c_char_p, []),
+        "va_version": (i32, []),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+
+
+def load(path: Optional[str] = None):
+    """Load the HIP library (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        p = path or LIB_PATH
+        if not os.path.exists(p):
+            raise RuntimeError(f"{p} is missing: build it with `python -m long_context_verify_tree_amd.build`")
+        lib = ctypes.CDLL(p)
+        _declare(lib)
+        _lib = lib
+    return _lib
+
+
+def _check(status: int):
+    if status != VA_OK:
+        raise VerifyAttnError(status, _lib.va_last_error().decode())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return VA_BF16
+    if t.dtype == torch.float32:
+        return VA_FP32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _strides3(t: torch.Tensor):
+    if t.dim() != 4 or t.stride(3) != 1:
+        raise ValueError("tensors must be 4-D with a unit innermost stride")
+    return (ctypes.c_int64 * 3)(*[t.stride(a) for a in range(3)])
+
+
+def make_desc(q, k_cache, v_cache, k_draft, v_draft, out, scale: Optional[float] = None) -> AttnDesc:
+    B, Hq, N, D = q.shape
+    Hkv = k_draft.shape[1]
+    L = k_cache.shape[2] if k_cache is not None else 0
+    d = AttnDesc()
+    d.B, d.Hq, d.Hkv, d.D, d.L, d.N = B, Hq, Hkv, D, L, N
+    d.dtype = _dtype_code(q)
+    d.scale = 0.0 if scale is None else float(scale)
+    d.q_stride = _strides3(q)
+    zero = (ctypes.c_int64 * 3)(0, 0, 0)
+    d.kc_stride = _strides3(k_cache) if k_cache is not None else zero
+    d.vc_stride = _strides3(v_cache) if v_cache is not None else zero
+    d.kd_stride = _strides3(k_draft)
+    d.vd_stride = _strides3(v_draft)
+    d.o_stride = _strides3(out)
+    return d
+
+
+def _check_inputs(q, k_cache, v_cache, k_draft, v_draft, parent):
+    ts = [t for t in (q, k_cache, v_cache, k_draft, v_draft) if t is not None]
+    dev = q.device
+    for t in ts:
+        if t.device != dev or t.dtype != q.dtype:
+            raise ValueError("q, caches and drafts must share device and dtype")
+    if dev.type != "cuda":
+        raise ValueError("tensors must live on a HIP device")
+    B, Hq, N, D = q.shape
+    Hkv = k_draft.shape[1]
+    if k_draft.shape != (B, Hkv, N, D) or v_draft.shape != (B, Hkv, N, D):
+        raise ValueError("k_draft / v_draft must be [B, Hkv, N, D]")
+    if k_cache is not None and (k_cache.shape[:2] != (B, Hkv) or k_cache.shape[3] != D
+                                or v_cache.shape != k_cache.shape):
+        raise ValueError("k_cache / v_cache must be [B, Hkv, L, D]")
+    if parent.shape != (B, N) or parent.dtype != torch.int32 or not parent.is_contiguous():
+        raise ValueError("parent must be a contiguous int32 [B, N] tensor")
+
+
+def workspace_size(desc: AttnDesc, n_ctx: int) -> int:
+    load()
+    n = ctypes.c_size_t()
+    _check(_lib.va_attn_workspace_size(ctypes.byref(desc), n_ctx, ctypes.byref(n)))
+    return n.value
+
+
+def _workspace(desc, n_ctx, device, workspace):
+    need = workspace_size(desc, n_ctx)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=device)
+    return workspace
+
+
+def _outputs(q, out, lse, want_lse):
+    B, Hq, N, D = q.shape
+    if out is None:
+        out = torch.empty_like(q, memory_format=torch.contiguous_format)
+    if lse is None and want_lse:
+        lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
+    return out, lse
+
+
+def verify_attn_dense(q, k_cache, v_cache, k_draft, v_draft, parent, *, out=None, lse=None,
+                      scale: Optional[float] = None, workspace=None,
+                      want_lse: bool = True) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Dense verification attention; returns (out [B,Hq,N,D], lse [B,Hq,N] or None)."""
+    load()
+    _check_inputs(q, k_cache, v_cache, k_draft, v_draft, parent)
+    out, lse = _outputs(q, out, lse, want_lse)
+    desc = make_desc(q, k_cache, v_cache, k_draft, v_draft, out, scale)
+    ws = _workspace(desc, desc.L, q.device, workspace)
+    _check(_lib.verify_attn_dense(ctypes.byref(desc), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_draft),
+                                  _ptr(v_draft), _ptr(parent), _ptr(out), _ptr(lse), _ptr(ws),
+                                  ws.numel(), _stream(q.device)))
+    return out, lse
+
+
+def verify_attn_sparse(q, k_cache, v_cache, k_draft, v_draft, parent, verify_idx, *, out=None, lse=None,
+                       scale: Optional[float] = None, workspace=None,
+                       want_lse: bool = True) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Sparse verification over verify_idx [B, K] int32; returns (out, lse)."""
+    load()
+    _check_inputs(q, k_cache, v_cache, k_draft, v_draft, parent)
+    if verify_idx.dtype != torch.int32 or verify_idx.dim() != 2 or verify_idx.stride(1) != 1:
+        raise ValueError("verify_idx must be int32 [B, K] with unit column stride")
+    K = verify_idx.shape[1]
+    out, lse = _outputs(q, out, lse, want_lse)
+    desc = make_desc(q, k_cache, v_cache, k_draft, v_draft, out, scale)
+    ws = _workspace(desc, K, q.device, workspace)
+    _check(_lib.verify_attn_sparse(ctypes.byref(desc), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_draft),
+                                   _ptr(v_draft), _ptr(parent), _ptr(verify_idx), K,
+                                   verify_idx.stride(0) if K else 0, _ptr(out), _ptr(lse), _ptr(ws),
+                                   ws.numel(), _stream(q.device)))
+    return out, lse
+
+
+def verify_attn_partials(desc: AttnDesc, q, k_cache, v_cache, k_draft, v_draft, parent, workspace,
+                         verify_idx=None):
+    """First stage only (split partials + tree partial) into ``workspace``."""
+    load()
+    K = verify_idx.shape[1] if verify_idx is not None else desc.L
+    stride = verify_idx.stride(0) if verify_idx is not None else 0
+    _check(_lib.verify_attn_partials(ctypes.byref(desc), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_draft),
+                                     _ptr(v_draft), _ptr(parent), _ptr(verify_idx), K, stride, _ptr(workspace),
+                                     workspace.numel(), _stream(q.device)))
+
+
+def verify_attn_merge(desc: AttnDesc, n_ctx: int, out, lse, workspace):
+    """Second stage only: log-sum-exp merge of the partials in ``workspace``."""
+    load()
+    _check(_lib.verify_attn_merge(ctypes.byref(desc), n_ctx, _ptr(out), _ptr(lse), _ptr(workspace),
+                                  workspace.numel(), _stream(out.device)))
+
+
+def select_workspace_size(B: int, L: int) -> int:
+    load()
+    n = ctypes.c_size_t()
+    _check(_lib.va_select_workspace_size(B, L, ctypes.byref(n)))
+    return n.value
+
+
+def select_verify_set(draft_score, target_score, *, sink: int, window: int, top_m: int, budget: int,
+                      out=None, workspace=None) -> torch.Tensor:
+    """I_verify per sequence: int32 [B, min(budget, L)], ascending."""
+    load()
+    if draft_score.shape != target_score.shape or draft_score.dim() != 2:
+        raise ValueError("scores must both be [B, L]")
+    if draft_score.dtype != torch.float32 or target_score.dtype != torch.float32:
+        raise ValueError("scores must be float32")
+    if draft_score.stride(1) != 1 or target_score.stride(1) != 1 or draft_score.stride(0) != target_score.stride(0):
+        raise ValueError("score rows must be contiguous with a common row stride")
+    B, L = draft_score.shape
+    k_out = min(budget, L)
+    if out is None:
+        out = torch.empty((B, k_out), dtype=torch.int32, device=draft_score.device)
+    need = select_workspace_size(B, L)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=draft_score.device)
+    _check(_lib.select_verify_set(_ptr(draft_score), _ptr(target_score), B, L, draft_score.stride(0) if B else L,
+                                  sink, window, top_m, budget, _ptr(out), _ptr(workspace),
+                                  workspace.numel() if workspace is not None else 0,
+                                  _stream(draft_score.device)))
+    return out

@@ -18,6 +18,6 @@ def gpu_lib():
     import torch
     if not torch.cuda.is_available():
         pytest.fail("GPU test collected on a machine without a GPU")
-    from long_context_verify_tree_amd import _lib
-    _lib.load()
-    return _lib
+    from long_context_verify_tree_amd import ops
+    ops.load()
+    return ops

@@ -1,0 +1,162 @@
+"""C-ABI checks that need no GPU: the library loads, exports every entry point
+declared in include/verify_attn.h, and rejects malformed arguments on the host
+with the documented status codes (before any HIP call is made)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "verify_attn.h")
+
+
+@pytest.fixture(scope="module")
+def ops():
+    from long_context_verify_tree_amd import ops as o
+    if not os.path.exists(o.LIB_PATH):
+        pytest.fail("libverify_attn.so is not built (run __graft_entry__.build())")
+    o.load()
+    return o
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s+\*?([A-Za-z_][A-Za-z0-9_]*)\s*\(",
+                       text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for want in ("verify_attn_dense", "verify_attn_sparse", "select_verify_set", "verify_attn_partials",
+                 "verify_attn_merge", "va_attn_workspace_size", "va_select_workspace_size", "va_status_str",
+                 "va_last_error", "va_version"):
+        assert want in names
+
+
+def test_library_exports_every_declared_symbol(ops):
+    lib = ctypes.CDLL(ops.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_single_hip_runtime_in_process(ops):
+    maps = [l.split()[-1] for l in open("/proc/self/maps") if "libamdhip64" in l]
+    assert len(set(maps)) == 1, set(maps)
+
+
+def test_status_strings(ops):
+    lib = ops._lib
+    assert lib.va_status_str(0) == b"ok"
+    assert b"workspace" in lib.va_status_str(3)
+    assert lib.va_version() >= 100
+
+
+def good_desc(ops, B=2, Hq=8, Hkv=2, D=128, L=1000, N=8, dtype=1):
+    d = ops.AttnDesc()
+    d.B, d.Hq, d.Hkv, d.D, d.L, d.N, d.dtype, d.scale = B, Hq, Hkv, D, L, N, dtype, 0.0
+    d.q_stride = (ctypes.c_int64 * 3)(Hq * N * D, N * D, D)
+    d.kc_stride = (ctypes.c_int64 * 3)(Hkv * L * D, L * D, D)
+    d.vc_stride = (ctypes.c_int64 * 3)(Hkv * L * D, L * D, D)
+    d.kd_stride = (ctypes.c_int64 * 3)(Hkv * N * D, N * D, D)
+    d.vd_stride = (ctypes.c_int64 * 3)(Hkv * N * D, N * D, D)
+    d.o_stride = (ctypes.c_int64 * 3)(Hq * N * D, N * D, D)
+    return d
+
+
+def ws_size(ops, d, n):
+    out = ctypes.c_size_t()
+    st = ops._lib.va_attn_workspace_size(ctypes.byref(d) if d is not None else None, n, ctypes.byref(out))
+    return st, out.value
+
+
+def test_workspace_size_and_validation(ops):
+    d = good_desc(ops)
+    st, n = ws_size(ops, d, d.L)
+    assert st == ops.VA_OK and n > 0
+    st0, n0 = ws_size(ops, d, 0)
+    assert st0 == ops.VA_OK and 0 < n0 < n
+    assert ws_size(ops, None, 10)[0] == ops.VA_EINVAL
+    assert ws_size(ops, d, d.L + 1)[0] == ops.VA_EINVAL
+    for field, val, code in (("Hkv", 3, ops.VA_EINVAL), ("D", 96, ops.VA_EUNSUPPORTED), ("N", 0, ops.VA_EINVAL),
+                             ("N", 257, ops.VA_EUNSUPPORTED), ("L", -1, ops.VA_EINVAL), ("B", 0, ops.VA_EINVAL),
+                             ("dtype", 7, ops.VA_EINVAL), ("scale", float("nan"), ops.VA_EINVAL)):
+        bad = good_desc(ops)
+        setattr(bad, field, val)
+        assert ws_size(ops, bad, 0)[0] == code, field
+        assert ops._lib.va_last_error() != b""
+    bad = good_desc(ops)
+    bad.kc_stride = (ctypes.c_int64 * 3)(2 * 1000 * 128, 1000 * 128, 100)   # rows not 16-byte aligned
+    assert ws_size(ops, bad, 0)[0] == ops.VA_EINVAL
+
+
+FAKE = ctypes.c_void_p(0x100000)   # never dereferenced: every call below fails validation first
+
+
+def dense(ops, d, ws_bytes, **over):
+    a = dict(q=FAKE, kc=FAKE, vc=FAKE, kd=FAKE, vd=FAKE, parent=FAKE, out=FAKE, lse=None, ws=FAKE)
+    a.update(over)
+    return ops._lib.verify_attn_dense(ctypes.byref(d) if d is not None else None, a["q"], a["kc"], a["vc"], a["kd"],
+                                      a["vd"], a["parent"], a["out"], a["lse"], a["ws"], ws_bytes, None)
+
+
+def test_dense_rejects_before_launch(ops):
+    d = good_desc(ops)
+    _, need = ws_size(ops, d, d.L)
+    assert dense(ops, None, need) == ops.VA_EINVAL
+    assert dense(ops, d, need - 1) == ops.VA_EWORKSPACE
+    assert dense(ops, d, need, ws=None) == ops.VA_EWORKSPACE
+    assert dense(ops, d, need, q=None) == ops.VA_EINVAL
+    assert dense(ops, d, need, out=None) == ops.VA_EINVAL
+    assert dense(ops, d, need, parent=None) == ops.VA_EINVAL
+    assert dense(ops, d, need, kc=None) == ops.VA_EINVAL
+    assert dense(ops, d, need, q=ctypes.c_void_p(0x100002)) == ops.VA_EINVAL   # misaligned base
+    d.D = 80
+    assert dense(ops, d, need) == ops.VA_EUNSUPPORTED
+
+
+def test_sparse_rejects_before_launch(ops):
+    d = good_desc(ops)
+    lib = ops._lib
+
+    def sparse(K, stride, idx=FAKE, ws_bytes=1 << 30):
+        return lib.verify_attn_sparse(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, idx, K, stride, FAKE, None,
+                                      FAKE, ws_bytes, None)
+    assert sparse(d.L + 1, d.L + 1) == ops.VA_EINVAL
+    assert sparse(-1, 10) == ops.VA_EINVAL
+    assert sparse(100, 99) == ops.VA_EINVAL
+    assert sparse(100, 100, idx=None) == ops.VA_EINVAL
+    assert sparse(100, 100, ws_bytes=16) == ops.VA_EWORKSPACE
+
+
+def select(ops, B, L, ld, sink, window, m, budget, out=FAKE, ds=FAKE, ws=None, ws_bytes=0):
+    return ops._lib.select_verify_set(ds, FAKE, B, L, ld, sink, window, m, budget, out, ws, ws_bytes, None)
+
+
+def test_select_rejects_before_launch(ops):
+    assert select(ops, 2, 1000, 999, 4, 16, 10, 100) == ops.VA_EINVAL            # ld < L
+    assert select(ops, 2, 1000, 1000, 4, 16, 10, 19) == ops.VA_EINVAL            # budget < sink + window
+    assert select(ops, 2, 1000, 1000, -1, 16, 10, 100) == ops.VA_EINVAL
+    assert select(ops, 2, 1000, 1000, 4, 16, 10, 100, out=None) == ops.VA_EINVAL
+    assert select(ops, 2, 1000, 1000, 4, 16, 10, 100, ds=None) == ops.VA_EINVAL
+    assert select(ops, 1, (1 << 20) + 1, (1 << 20) + 1, 4, 16, 10, 100) == ops.VA_EUNSUPPORTED
+    # nothing to do: OK without a launch
+    assert select(ops, 0, 1000, 1000, 4, 16, 10, 100) == ops.VA_OK
+    assert select(ops, 2, 1000, 1000, 4, 16, 10, 0, out=None) != ops.VA_EHIP
+    n = ctypes.c_size_t(99)
+    assert ops._lib.va_select_workspace_size(4, 131072, ctypes.byref(n)) == ops.VA_OK
+
+
+def test_product_path_does_not_touch_the_oracle():
+    """The binding and the HIP sources never import or include the oracle."""
+    pkg = os.path.join(ROOT, "long_context_verify_tree_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, f)).read()
+                bad = re.findall(r"^\s*(?:import\s+oracle|from\s+oracle|#\s*include\s*[<\"].*oracle)", text,
+                                 flags=re.M)
+                assert not bad, (os.path.join(dirpath, f), bad)
