@@ -140,6 +140,18 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(PartialParams p) {
     }
   }
 
+  // draft node of each of this lane's rows (tree mask lookup)
+  int node_of[RB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const int r = row0 + 32 * rb + n;
+    node_of[rb] = r < p.R ? r % p.N : 0;
+  }
+  if (!tree) {
+    // keep the (unused) mask words defined for the branch-free lookup below
+    for (int j = tid; j < kMaxN * kAncWords; j += kThreads) (&anc[0][0])[j] = ~0u;
+  }
+
   // ---- key range of this part
   const T* kbase;
   const T* vbase;
@@ -229,6 +241,12 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(PartialParams p) {
     const uint32_t vmask = vmask_next;
     if (t + kWaves < ntiles) load_tile(t + kWaves);  // in flight during the math below
 
+    // Visible keys of this tile per row, computed before the MFMAs so that no
+    // branch separates the S^T chain from the reads of its accumulators.
+    uint32_t key_bits[RB];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) key_bits[rb] = vmask & (tree ? anc[node_of[rb]][t & (kAncWords - 1)] : ~0u);
+
     // S^T = K_tile . Q^T
     f32x16 s[RB];
 #pragma unroll
@@ -256,12 +274,7 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(PartialParams p) {
     // mask, online softmax; s becomes P (unnormalised)
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
-      uint32_t bits = vmask;
-      if (tree) {
-        const int r = row0 + 32 * rb + n;
-        const int node = r < p.R ? r % p.N : 0;
-        bits &= anc[node][t];
-      }
+      const uint32_t bits = key_bits[rb];
       float tmax = -INFINITY;
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
