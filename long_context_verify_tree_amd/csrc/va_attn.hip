@@ -62,15 +62,22 @@ __device__ inline int xcd_remap(int x, int total) {
 
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Two wavefronts per SIMD where the registers allow it (one 32-row block):
+// twice the K/V bytes in flight per CU for the HBM-bound shapes.
 template <class T, int D, int RB, bool GATHER>
-__global__ __launch_bounds__(kThreads) void partial_kernel(PartialParams p) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(RB == 1 && sizeof(T) == 2 ? 2 : 1)))
+void partial_kernel(PartialParams p) {
   constexpr int ES = sizeof(T);
   constexpr int VEC = 16 / ES;                     // elements per 16-byte chunk
   constexpr int LDR = D + VEC;                     // LDS row stride (elements), 16 B pad
   constexpr int CPR = D / VEC;                     // chunks per key row
   constexpr int NCH = kTileKeys * CPR / 64;        // chunks per lane per tile (K or V)
-  constexpr int TILE_ELEMS = kTileKeys * LDR;
-  constexpr int WAVE_ELEMS = 2 * TILE_ELEMS;       // K tile then V tile
+  constexpr int TILE_ELEMS = kTileKeys * LDR;      // K tile, key-major rows
+  // V tile stored transposed (d-major rows of the tile's 32 keys) so an MFMA
+  // A operand of V^T is two 8-byte reads.  Row stride padded to spread banks.
+  constexpr int VT_LDR = (ES == 2) ? kTileKeys + 4 : kTileKeys + 1;
+  constexpr int VT_ELEMS = D * VT_LDR;
+  constexpr int WAVE_ELEMS = TILE_ELEMS + VT_ELEMS;  // K tile then V^T tile
   constexpr int TILES_BYTES = kWaves * WAVE_ELEMS * ES;
   constexpr int NDB = D / 32;                      // 32-wide d blocks of O^T
   constexpr int OACC = NDB * RB * 16;              // O^T accumulators per lane
@@ -79,7 +86,7 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(PartialParams p) {
   static_assert(NCH * 64 == kTileKeys * CPR, "tile must split evenly over a wavefront");
 
   __shared__ __attribute__((aligned(16))) unsigned char smem[SMEM_BYTES];
-  __shared__ uint32_t anc[kMaxN][kAncWords];
+  __shared__ uint32_t anc[32 * RB][kAncWords];   // ancestor bits of each row's draft node
   __shared__ int par[kMaxN];
   __shared__ float mbuf[kWaves][RB][32];
   __shared__ float lbuf[RB][64];
@@ -101,19 +108,23 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(PartialParams p) {
   const bool tree = part == p.n_ctx_splits;
   const int row0 = rt * 32 * RB;
 
-  // ---- ancestor bitmasks of the draft tree (tree part only)
+  // ---- ancestor bitmasks of the draft tree, one per row of this tile.
+  // Ctx parts fill them with ones so the mask lookup needs no branch.
   if (tree) {
     for (int j = tid; j < p.N; j += kThreads) par[j] = p.parent[(int64_t)b * p.N + j];
-    for (int j = tid; j < kMaxN * kAncWords; j += kThreads) (&anc[0][0])[j] = 0u;
+    for (int j = tid; j < 32 * RB * kAncWords; j += kThreads) (&anc[0][0])[j] = 0u;
     __syncthreads();
-    if (tid < p.N) {
-      int j = tid;
+    if (tid < 32 * RB && row0 + tid < p.R) {
+      int j = (row0 + tid) % p.N;
       for (int step = 0; step <= p.N && j >= 0; ++step) {
         anc[tid][j >> 5] |= 1u << (j & 31);
         int pj = par[j];
         j = (pj >= -1 && pj < j) ? pj : -1;  // malformed parents end the path
       }
     }
+    __syncthreads();
+  } else {
+    for (int j = tid; j < 32 * RB * kAncWords; j += kThreads) (&anc[0][0])[j] = ~0u;
     __syncthreads();
   }
 
@@ -138,18 +149,6 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(PartialParams p) {
         qop[rb][ks] = ok ? qrow[2 * ks + h] : 0.f;
       }
     }
-  }
-
-  // draft node of each of this lane's rows (tree mask lookup)
-  int node_of[RB];
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    const int r = row0 + 32 * rb + n;
-    node_of[rb] = r < p.R ? r % p.N : 0;
-  }
-  if (!tree) {
-    // keep the (unused) mask words defined for the branch-free lookup below
-    for (int j = tid; j < kMaxN * kAncWords; j += kThreads) (&anc[0][0])[j] = ~0u;
   }
 
   // ---- key range of this part
@@ -177,7 +176,7 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(PartialParams p) {
   const int ntiles = ke > kb ? (ke - kb + kTileKeys - 1) / kTileKeys : 0;
 
   T* kt = (T*)smem + wave * WAVE_ELEMS;
-  T* vt = kt + TILE_ELEMS;
+  T* vt = kt + TILE_ELEMS;   // V^T: vt[d * VT_LDR + key]
 
   u32x4 kreg[NCH], vreg[NCH];
   uint32_t vmask_next = 0;
@@ -194,23 +193,25 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(PartialParams p) {
 
   auto load_tile = [&](int t) {
     const int key0 = kb + kTileKeys * t;
+    // K: chunk c of lane -> (key kk, column col): 16-byte pieces of whole rows.
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
       const int chunk = lane + 64 * c;
       const int kk = chunk / CPR, col = chunk % CPR;
       bool ok;
       const int64_t pos = key_pos(key0 + kk, ok);
-      if (ok) {
-        kreg[c] = *(const u32x4*)(kbase + pos * kts + col * VEC);
-        vreg[c] = *(const u32x4*)(vbase + pos * vts + col * VEC);
-      } else {
-        kreg[c] = u32x4{0, 0, 0, 0};
-        vreg[c] = u32x4{0, 0, 0, 0};
-      }
+      kreg[c] = ok ? *(const u32x4*)(kbase + pos * kts + col * VEC) : u32x4{0, 0, 0, 0};
     }
-    bool mine;
-    key_pos(key0 + n, mine);
-    vmask_next = (uint32_t)__ballot(mine && h == 0);
+    // V: lane -> key (lane % 32), columns 2c + lane / 32, so the transposed
+    // LDS writes of one instruction cover consecutive keys of one d row.
+    bool vok;
+    const int64_t vpos = key_pos(key0 + n, vok);
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      const int col = 2 * c + h;
+      vreg[c] = vok ? *(const u32x4*)(vbase + vpos * vts + col * VEC) : u32x4{0, 0, 0, 0};
+    }
+    vmask_next = (uint32_t)__ballot(vok && h == 0);
   };
 
   // ---- online softmax state
@@ -236,7 +237,22 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(PartialParams p) {
       const int chunk = lane + 64 * cc;
       const int kk = chunk / CPR, col = chunk % CPR;
       *(u32x4*)(kt + kk * LDR + col * VEC) = kreg[cc];
-      *(u32x4*)(vt + kk * LDR + col * VEC) = vreg[cc];
+      // V^T: the VEC elements of this chunk go to rows d = (2cc + h) * VEC + e
+      const int d0 = (2 * cc + h) * VEC;
+      if constexpr (ES == 2) {
+        const uint32_t w[4] = {vreg[cc][0], vreg[cc][1], vreg[cc][2], vreg[cc][3]};
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          vt[(d0 + e) * VT_LDR + n] = (T)((w[e >> 1] >> (16 * (e & 1))) & 0xffffu);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          // (element copied to a scalar first: bit-casting a vector-element
+          // subscript directly yields element 0 with this compiler)
+          const uint32_t x = vreg[cc][e];
+          vt[(d0 + e) * VT_LDR + n] = __uint_as_float(x);
+        }
+      }
     }
     const uint32_t vmask = vmask_next;
     if (t + kWaves < ntiles) load_tile(t + kWaves);  // in flight during the math below
@@ -245,7 +261,7 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(PartialParams p) {
     // branch separates the S^T chain from the reads of its accumulators.
     uint32_t key_bits[RB];
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) key_bits[rb] = vmask & (tree ? anc[node_of[rb]][t & (kAncWords - 1)] : ~0u);
+    for (int rb = 0; rb < RB; ++rb) key_bits[rb] = vmask & anc[32 * rb + n][t & (kAncWords - 1)];
 
     // S^T = K_tile . Q^T
     f32x16 s[RB];
@@ -256,7 +272,8 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(PartialParams p) {
     if constexpr (ES == 2) {
 #pragma unroll
       for (int ks = 0; ks < D / 16; ++ks) {
-        const bf16x8 a = __builtin_bit_cast(bf16x8, *(const u32x4*)(kt + n * LDR + 16 * ks + 8 * h));
+        const u32x4 kv = *(const u32x4*)(kt + n * LDR + 16 * ks + 8 * h);
+        const bf16x8 a = __builtin_bit_cast(bf16x8, kv);
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb)
           s[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qop[rb][ks], s[rb], 0, 0, 0);
@@ -313,12 +330,12 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(PartialParams p) {
           for (int j = 0; j < 8; ++j) pb[rb][j] = (__bf16)s[rb][8 * ks + j];
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
-          bf16x8 a;
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            const int key = 16 * ks + 8 * (j >> 2) + 4 * h + (j & 3);
-            a[j] = __builtin_bit_cast(__bf16, vt[key * LDR + 32 * db + n]);
-          }
+          // k-slots j = 0..3: keys 16ks + 4h + j; j = 4..7: keys 16ks + 8 + 4h + (j - 4)
+          const T* vrow = vt + (32 * db + n) * VT_LDR + 16 * ks + 4 * h;
+          typedef uint32_t u32x2 __attribute__((ext_vector_type(2), __may_alias__));
+          const u32x2 lo = *(const u32x2*)(vrow);
+          const u32x2 hi = *(const u32x2*)(vrow + 8);
+          const bf16x8 a = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
 #pragma unroll
           for (int rb = 0; rb < RB; ++rb)
             o[rb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[rb], o[rb][db], 0, 0, 0);
@@ -330,7 +347,7 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(PartialParams p) {
         const int key = 8 * (e >> 2) + 4 * h + (e & 3);
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
-          const float a = vt[key * LDR + 32 * db + n];
+          const float a = vt[(32 * db + n) * VT_LDR + key];
 #pragma unroll
           for (int rb = 0; rb < RB; ++rb)
             o[rb][db] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, s[rb][e], o[rb][db], 0, 0, 0);
@@ -409,6 +426,10 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(PartialParams p) {
 
 template <class T, int D>
 __global__ __launch_bounds__(256) void merge_kernel(MergeParams p) {
+  // One wavefront per output row.  Lane s holds part s's log2-sum-exp; the
+  // maximum and the weight sum are wavefront shuffle reductions; the weights
+  // are broadcast with readlane, so the partial-row loads are independent of
+  // one another and stay in flight together.
   const int lane = threadIdx.x & 63;
   const int64_t prow = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (prow >= p.rows) return;
@@ -416,9 +437,10 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeParams p) {
   const int hq = (int)((prow / p.N) % p.Hq);
   const int64_t b = prow / ((int64_t)p.N * p.Hq);
   const float* lse2 = p.part_lse + prow * p.n_parts;
+  const int np = p.n_parts;
 
   float M = -INFINITY;
-  for (int s = lane; s < p.n_parts; s += 64) M = fmaxf(M, lse2[s]);
+  for (int s = lane; s < np; s += 64) M = fmaxf(M, lse2[s]);
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
   const float muse = M == -INFINITY ? 0.f : M;
@@ -428,13 +450,32 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeParams p) {
 #pragma unroll
   for (int e = 0; e < PER; ++e) acc[e] = 0.f;
   float wsum = 0.f;
-  const float* po = p.part_o + prow * p.n_parts * D + lane * PER;
-  for (int s = 0; s < p.n_parts; ++s) {
-    const float w = exp2f(lse2[s] - muse);
-    wsum += w;
-    if (w != 0.f) {
+  const float* po = p.part_o + prow * np * D + lane * PER;
+  for (int s0 = 0; s0 < np; s0 += 64) {
+    const int cnt = min(64, np - s0);
+    const float wl = lane < cnt ? exp2f(lse2[s0 + lane] - muse) : 0.f;
+    float ws = wl;
 #pragma unroll
-      for (int e = 0; e < PER; ++e) acc[e] = fmaf(w, po[(int64_t)s * D + e], acc[e]);
+    for (int off = 32; off >= 1; off >>= 1) ws += __shfl_xor(ws, off);
+    wsum += ws;
+    int s = 0;
+    for (; s + 8 <= cnt; s += 8) {
+      float v[8][PER];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+#pragma unroll
+        for (int e = 0; e < PER; ++e) v[u][e] = po[(int64_t)(s0 + s + u) * D + e];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const float w = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wl), s + u));
+#pragma unroll
+        for (int e = 0; e < PER; ++e) acc[e] = fmaf(w, v[u][e], acc[e]);
+      }
+    }
+    for (; s < cnt; ++s) {
+      const float w = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wl), s));
+#pragma unroll
+      for (int e = 0; e < PER; ++e) acc[e] = fmaf(w, po[(int64_t)(s0 + s) * D + e], acc[e]);
     }
   }
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
