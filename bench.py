@@ -50,6 +50,27 @@ def algorithmic(cfg, n_ctx: int, sparse: bool):
                 flops=flops)
 
 
+KERNEL_SOURCE = os.path.join(ROOT, "long_context_verify_tree_amd", "csrc", "va_attn.hip")
+
+
+def committed_traffic(workload: str):
+    """HBM bytes per partial-kernel launch from the committed rocprofv3 counter
+    summary, or None if there is none or the kernel source changed since."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"partial_kernel_{workload}.md")
+    if not os.path.exists(path):
+        return None, None
+    fields = {}
+    for line in open(path):
+        if ":" in line and line.startswith("- "):
+            k, v = line[2:].split(":", 1)
+            fields[k.strip()] = v.strip().strip("`")
+    digest = hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()
+    if fields.get("kernel source sha256") != digest or "traffic bytes per launch" not in fields:
+        return None, os.path.relpath(path, ROOT) + " (stale: kernel changed since the counters were taken)"
+    return int(float(fields["traffic bytes per launch"])), os.path.relpath(path, ROOT)
+
+
 def cpu_baseline(cfg, x, budget_s: float):
     """The oracle, untouched, on as many (sequence, KV-head group) slabs of the
     benchmarked inputs as fit the time budget."""
@@ -94,6 +115,8 @@ def main():
     ap.add_argument("--copies", type=int, default=0, help="input copies rotated over steps (0: auto)")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calib-gib", type=float, default=0.0,
+                    help="after timing, run a plain device copy of this many GiB (HBM counter calibration)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -206,6 +229,15 @@ def main():
                    "verify": "sparse" if sparse else "dense", "n_ctx_keys": n_ctx},
         "roofline": roof,
     }
+    roof["traffic"], roof["traffic_source"] = committed_traffic(cfg.name)
+    if args.copy_calib_gib > 0:
+        n = int(args.copy_calib_gib * (1 << 30))
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle sample", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(cfg, x, args.cpu_budget)

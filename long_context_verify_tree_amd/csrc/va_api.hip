@@ -66,10 +66,13 @@ va::Plan make_plan(const va_attn_desc* d, int32_t n_ctx) {
   const int rows_per_tile = 32 * pl.rb;
   pl.row_tiles = (R + rows_per_tile - 1) / rows_per_tile;
   const int64_t pairs = (int64_t)d->B * d->Hkv * pl.row_tiles;
-  // Enough context workgroups to cover the chip a few times over, but no
-  // split shorter than 512 keys: every split costs one partial row per query
-  // row in the workspace.
-  const int64_t target_groups = 1024;
+  // Enough context workgroups to fill every CU slot, but no split shorter
+  // than 512 keys: every split costs one partial row per query row in the
+  // workspace.
+#ifndef VA_TARGET_GROUPS
+#define VA_TARGET_GROUPS 512
+#endif
+  const int64_t target_groups = VA_TARGET_GROUPS;
   int64_t want_splits = (target_groups + pairs - 1) / pairs;
   if (want_splits < 1) want_splits = 1;
   int64_t len = n_ctx > 0 ? (n_ctx + want_splits - 1) / want_splits : 128;

@@ -32,6 +32,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include <hip/hip_runtime.h>
 
 #include "va_internal.h"
@@ -44,6 +46,8 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 // 16-byte vector used for every global/LDS move.  may_alias: LDS tiles are
 // written through this type and read back as bf16 / float elements.
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4), __may_alias__));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2), __may_alias__));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
@@ -62,30 +66,50 @@ __device__ inline int xcd_remap(int x, int total) {
 
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Two wavefronts per SIMD where the registers allow it (one 32-row block):
-// twice the K/V bytes in flight per CU for the HBM-bound shapes.
+// Bank-conflict swizzle of the 16-byte chunks of a key row in LDS.
+template <int CPR>
+__device__ inline int swz(int row, int chunk) {
+  return chunk ^ (row & (CPR - 1));
+}
+
+#ifndef VA_RING_TILES
+#define VA_RING_TILES 2
+#endif
+template <int RB, int ES, int D>
+struct KernelShape {
+  // The HBM-bound shapes (bf16, one 32-row block) run one wavefront per SIMD
+  // with a ring of register tiles in flight; registers are the larger
+  // buffer on a CU (512 KiB vs 160 KiB of LDS).  D = 64 rows are half as
+  // long, so a two-tile ring fits as well.
+  static constexpr bool hbm_shape = RB == 1 && ES == 2;
+  static constexpr int prefetch = hbm_shape ? (D == 128 ? VA_RING_TILES : 2) : 1;
+  static constexpr int waves_per_eu = hbm_shape && prefetch == 1 ? 2 : 1;
+};
+
 template <class T, int D, int RB, bool GATHER>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(RB == 1 && sizeof(T) == 2 ? 2 : 1)))
+__global__ __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu(KernelShape<RB, sizeof(T), D>::waves_per_eu)))
 void partial_kernel(PartialParams p) {
   constexpr int ES = sizeof(T);
+  constexpr bool BF = ES == 2;
+  constexpr int PF = KernelShape<RB, ES, D>::prefetch;
   constexpr int VEC = 16 / ES;                     // elements per 16-byte chunk
-  constexpr int LDR = D + VEC;                     // LDS row stride (elements), 16 B pad
   constexpr int CPR = D / VEC;                     // chunks per key row
   constexpr int NCH = kTileKeys * CPR / 64;        // chunks per lane per tile (K or V)
-  constexpr int TILE_ELEMS = kTileKeys * LDR;      // K tile, key-major rows
-  // V tile stored transposed (d-major rows of the tile's 32 keys) so an MFMA
-  // A operand of V^T is two 8-byte reads.  Row stride padded to spread banks.
-  constexpr int VT_LDR = (ES == 2) ? kTileKeys + 4 : kTileKeys + 1;
-  constexpr int VT_ELEMS = D * VT_LDR;
-  constexpr int WAVE_ELEMS = TILE_ELEMS + VT_ELEMS;  // K tile then V^T tile
+  constexpr int TILE_ELEMS = kTileKeys * D;        // row-major, chunk-swizzled
+  constexpr int WAVE_ELEMS = 2 * TILE_ELEMS;       // K tile then V tile
   constexpr int TILES_BYTES = kWaves * WAVE_ELEMS * ES;
+  constexpr int QROWS = 32 * RB;
+  constexpr int Q_BYTES = BF ? QROWS * D * 2 : 16; // bf16 queries are read from LDS
   constexpr int NDB = D / 32;                      // 32-wide d blocks of O^T
   constexpr int OACC = NDB * RB * 16;              // O^T accumulators per lane
   constexpr int OBUF_BYTES = OACC * 64 * 4;
   constexpr int SMEM_BYTES = TILES_BYTES > OBUF_BYTES ? TILES_BYTES : OBUF_BYTES;
   static_assert(NCH * 64 == kTileKeys * CPR, "tile must split evenly over a wavefront");
+  static_assert((CPR & (CPR - 1)) == 0, "chunks per row must be a power of two");
 
   __shared__ __attribute__((aligned(16))) unsigned char smem[SMEM_BYTES];
+  __shared__ __attribute__((aligned(16))) unsigned char qsm[Q_BYTES];
   __shared__ uint32_t anc[32 * RB][kAncWords];   // ancestor bits of each row's draft node
   __shared__ int par[kMaxN];
   __shared__ float mbuf[kWaves][RB][32];
@@ -108,6 +132,22 @@ void partial_kernel(PartialParams p) {
   const bool tree = part == p.n_ctx_splits;
   const int row0 = rt * 32 * RB;
 
+  auto q_row_ptr = [&](int r) -> const T* {
+    const int g = r / p.N, i = r % p.N;
+    return (const T*)p.q + (int64_t)b * p.qs[0] + (int64_t)(kvh * p.G + g) * p.qs[1] + (int64_t)i * p.qs[2];
+  };
+
+  // ---- bf16 queries of this row tile into LDS (row-major, chunk-swizzled)
+  if constexpr (BF) {
+    T* qs = (T*)qsm;
+    for (int c = tid; c < QROWS * CPR; c += kThreads) {
+      const int r = c / CPR, col = c % CPR;
+      u32x4 v = u32x4{0, 0, 0, 0};
+      if (row0 + r < p.R) v = *(const u32x4*)(q_row_ptr(row0 + r) + col * VEC);
+      *(u32x4*)(qs + r * D + swz<CPR>(r, col) * VEC) = v;
+    }
+  }
+
   // ---- ancestor bitmasks of the draft tree, one per row of this tile.
   // Ctx parts fill them with ones so the mask lookup needs no branch.
   if (tree) {
@@ -122,32 +162,22 @@ void partial_kernel(PartialParams p) {
         j = (pj >= -1 && pj < j) ? pj : -1;  // malformed parents end the path
       }
     }
-    __syncthreads();
   } else {
     for (int j = tid; j < 32 * RB * kAncWords; j += kThreads) (&anc[0][0])[j] = ~0u;
-    __syncthreads();
   }
+  __syncthreads();
 
-  // ---- queries of this lane's rows as MFMA B operands (Q^T)
-  constexpr int QOPS = (ES == 2) ? D / 16 : D / 2;
-  typedef typename std::conditional<ES == 2, bf16x8, float>::type QOp;
-  QOp qop[RB][QOPS];
+  // ---- fp32 queries stay in registers as MFMA B operands (Q^T)
+  constexpr int QREG = BF ? 1 : D / 2;
+  float qf[RB][QREG];
+  if constexpr (!BF) {
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    const int r = row0 + 32 * rb + n;
-    const bool ok = r < p.R;
-    const int g = ok ? r / p.N : 0;
-    const int i = ok ? r % p.N : 0;
-    const T* qrow = (const T*)p.q + (int64_t)b * p.qs[0] + (int64_t)(kvh * p.G + g) * p.qs[1] +
-                    (int64_t)i * p.qs[2];
+    for (int rb = 0; rb < RB; ++rb) {
+      const int r = row0 + 32 * rb + n;
+      const bool ok = r < p.R;
+      const T* qrow = q_row_ptr(ok ? r : 0);
 #pragma unroll
-    for (int ks = 0; ks < QOPS; ++ks) {
-      if constexpr (ES == 2) {
-        u32x4 v = ok ? *(const u32x4*)(qrow + 16 * ks + 8 * h) : u32x4{0, 0, 0, 0};
-        qop[rb][ks] = __builtin_bit_cast(bf16x8, v);
-      } else {
-        qop[rb][ks] = ok ? qrow[2 * ks + h] : 0.f;
-      }
+      for (int ks = 0; ks < QREG; ++ks) qf[rb][ks] = ok ? qrow[2 * ks + h] : 0.f;
     }
   }
 
@@ -168,50 +198,65 @@ void partial_kernel(PartialParams p) {
     vbase = (const T*)p.vc + (int64_t)b * p.vcs[0] + (int64_t)kvh * p.vcs[1];
     kts = p.kcs[2];
     vts = p.vcs[2];
-    kb = part * p.split_len;
-    ke = min(p.n_ctx, kb + p.split_len);
+    kb = 0;
+    ke = p.n_ctx;
   }
   const bool gather = GATHER && !tree;
   const int32_t* idx_row = GATHER ? p.idx + (int64_t)b * p.idx_stride : nullptr;
   const int ntiles = ke > kb ? (ke - kb + kTileKeys - 1) / kTileKeys : 0;
+  // Context tiles are dealt out round-robin: at step k the S splits' waves
+  // of this (sequence, kv head) read tiles 4(kS + part) + wave, one
+  // contiguous window of 4S tiles, which keeps DRAM accesses local.  The
+  // tree part walks its (at most 8) tiles with its four waves.
+  const int tstep = tree ? kWaves : kWaves * p.n_ctx_splits;
+  const int tfirst = tree ? wave : kWaves * part + wave;
 
   T* kt = (T*)smem + wave * WAVE_ELEMS;
-  T* vt = kt + TILE_ELEMS;   // V^T: vt[d * VT_LDR + key]
+  T* vt = kt + TILE_ELEMS;
 
-  u32x4 kreg[NCH], vreg[NCH];
-  uint32_t vmask_next = 0;
+  u32x4 kreg[PF][NCH], vreg[PF][NCH];
+  uint32_t vmask[PF];
 
+  // Position of context key `key` (< ke) in the cache; `ok` is false for
+  // keys past the end and for gathered indices outside [0, L).  Loads are
+  // issued for every lane (invalid ones read row 0, which always exists when
+  // a part has keys) and zeroed afterwards, so the load stream has no
+  // branches and the wait counts before each staged chunk stay partial.
   auto key_pos = [&](int key, bool& ok) -> int64_t {
     ok = key < ke;
-    if (gather && ok) {
-      const int ix = idx_row[key];
-      ok = (unsigned)ix < (unsigned)p.L;
-      return ix;
+    int64_t pos = ok ? key : 0;
+    if constexpr (GATHER) {
+      if (gather) {
+        const int ix = idx_row[ok ? key : 0];
+        ok = ok && (unsigned)ix < (unsigned)p.L;
+        pos = ok ? ix : 0;
+      }
     }
-    return key;
+    return pos;
   };
 
-  auto load_tile = [&](int t) {
-    const int key0 = kb + kTileKeys * t;
-    // K: chunk c of lane -> (key kk, column col): 16-byte pieces of whole rows.
+  // chunk c of a lane covers key row (lane + 64c) / CPR, column (lane + 64c) % CPR.
+  // The raw chunk stays in registers; whether it holds a real key is kept
+  // as bit c of `okbits` and applied when the chunk is staged, so nothing
+  // waits on the load before then.
+  auto load_chunk = [&](int t, int c, u32x4& kr, u32x4& vr, uint32_t& okbits) {
+    const int chunk = lane + 64 * c;
+    const int kk = chunk / CPR, col = chunk % CPR;
+    bool ok;
+    const int64_t pos = key_pos(kb + kTileKeys * t + kk, ok);
+    kr = *(const u32x4*)(kbase + pos * kts + col * VEC);
+    vr = *(const u32x4*)(vbase + pos * vts + col * VEC);
+    okbits = (okbits & ~(1u << c)) | ((uint32_t)ok << c);
+  };
+  auto tile_mask = [&](int t) -> uint32_t {
+    bool mine;
+    key_pos(kb + kTileKeys * t + n, mine);
+    return (uint32_t)__ballot(mine && h == 0);
+  };
+  auto load_tile = [&](int t, u32x4 (&kr)[NCH], u32x4 (&vr)[NCH], uint32_t& vm, uint32_t& okbits) {
 #pragma unroll
-    for (int c = 0; c < NCH; ++c) {
-      const int chunk = lane + 64 * c;
-      const int kk = chunk / CPR, col = chunk % CPR;
-      bool ok;
-      const int64_t pos = key_pos(key0 + kk, ok);
-      kreg[c] = ok ? *(const u32x4*)(kbase + pos * kts + col * VEC) : u32x4{0, 0, 0, 0};
-    }
-    // V: lane -> key (lane % 32), columns 2c + lane / 32, so the transposed
-    // LDS writes of one instruction cover consecutive keys of one d row.
-    bool vok;
-    const int64_t vpos = key_pos(key0 + n, vok);
-#pragma unroll
-    for (int c = 0; c < NCH; ++c) {
-      const int col = 2 * c + h;
-      vreg[c] = vok ? *(const u32x4*)(vbase + vpos * vts + col * VEC) : u32x4{0, 0, 0, 0};
-    }
-    vmask_next = (uint32_t)__ballot(vok && h == 0);
+    for (int c = 0; c < NCH; ++c) load_chunk(t, c, kr[c], vr[c], okbits);
+    vm = tile_mask(t);
   };
 
   // ---- online softmax state
@@ -228,40 +273,15 @@ void partial_kernel(PartialParams p) {
   }
   const float c = p.c;
 
-  int t = wave;
-  if (t < ntiles) load_tile(t);
-  for (; t < ntiles; t += kWaves) {
-    // stage the fetched tile in this wavefront's LDS tile
-#pragma unroll
-    for (int cc = 0; cc < NCH; ++cc) {
-      const int chunk = lane + 64 * cc;
-      const int kk = chunk / CPR, col = chunk % CPR;
-      *(u32x4*)(kt + kk * LDR + col * VEC) = kreg[cc];
-      // V^T: the VEC elements of this chunk go to rows d = (2cc + h) * VEC + e
-      const int d0 = (2 * cc + h) * VEC;
-      if constexpr (ES == 2) {
-        const uint32_t w[4] = {vreg[cc][0], vreg[cc][1], vreg[cc][2], vreg[cc][3]};
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          vt[(d0 + e) * VT_LDR + n] = (T)((w[e >> 1] >> (16 * (e & 1))) & 0xffffu);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          // (element copied to a scalar first: bit-casting a vector-element
-          // subscript directly yields element 0 with this compiler)
-          const uint32_t x = vreg[cc][e];
-          vt[(d0 + e) * VT_LDR + n] = __uint_as_float(x);
-        }
-      }
-    }
-    const uint32_t vmask = vmask_next;
-    if (t + kWaves < ntiles) load_tile(t + kWaves);  // in flight during the math below
-
-    // Visible keys of this tile per row, computed before the MFMAs so that no
-    // branch separates the S^T chain from the reads of its accumulators.
+  // One tile of attention.  MASKED (a compile-time tag) handles tiles with
+  // invisible keys (the last context tile, the tree part); whole context
+  // tiles take the unmasked instance.  The choice is made before the MFMAs,
+  // so no branch separates the S^T chain from the reads of its accumulators.
+  auto compute = [&](int t, uint32_t vm, auto masked_tag) {
+    constexpr bool MASKED = decltype(masked_tag)::value;
     uint32_t key_bits[RB];
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) key_bits[rb] = vmask & anc[32 * rb + n][t & (kAncWords - 1)];
+    for (int rb = 0; rb < RB; ++rb) key_bits[rb] = MASKED ? vm & anc[32 * rb + n][t & (kAncWords - 1)] : ~0u;
 
     // S^T = K_tile . Q^T
     f32x16 s[RB];
@@ -269,41 +289,63 @@ void partial_kernel(PartialParams p) {
     for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
       for (int e = 0; e < 16; ++e) s[rb][e] = 0.f;
-    if constexpr (ES == 2) {
+    if constexpr (BF) {
+      const T* qs = (const T*)qsm;
 #pragma unroll
       for (int ks = 0; ks < D / 16; ++ks) {
-        const u32x4 kv = *(const u32x4*)(kt + n * LDR + 16 * ks + 8 * h);
+        // keep the scheduler from hoisting every operand read of the tile
+        // (register budget of two wavefronts per SIMD)
+        if (ks % 2 == 0) __builtin_amdgcn_sched_barrier(0);
+        const u32x4 kv = *(const u32x4*)(kt + n * D + swz<CPR>(n, 2 * ks + h) * VEC);
         const bf16x8 a = __builtin_bit_cast(bf16x8, kv);
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb)
-          s[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qop[rb][ks], s[rb], 0, 0, 0);
+        for (int rb = 0; rb < RB; ++rb) {
+          const int qr = 32 * rb + n;
+          const u32x4 qv = *(const u32x4*)(qs + qr * D + swz<CPR>(qr, 2 * ks + h) * VEC);
+          s[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8, qv), s[rb], 0, 0, 0);
+        }
       }
     } else {
 #pragma unroll
       for (int ks = 0; ks < D / 2; ++ks) {
-        const float a = kt[n * LDR + 2 * ks + h];
+        const int d = 2 * ks + h;
+        const float a = kt[n * D + swz<CPR>(n, d / VEC) * VEC + d % VEC];
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb)
-          s[rb] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, qop[rb][ks], s[rb], 0, 0, 0);
+          s[rb] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, qf[rb][ks], s[rb], 0, 0, 0);
       }
     }
 
-    // mask, online softmax; s becomes P (unnormalised)
+    // mask, online softmax; s becomes P (unnormalised).  The running max of
+    // a row only moves when this tile's max exceeds it by more than 2^8 in
+    // exp2 units (lazy rescaling): otherwise P is taken against the stale max
+    // (values <= 256, exact enough in fp32 and bf16) and O is left alone.
+    // The rescale is one wave-uniform branch, rarely taken after the first
+    // tiles.
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
-      const uint32_t bits = key_bits[rb];
       float tmax = -INFINITY;
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const int key = 8 * (e >> 2) + 4 * h + (e & 3);
-        if (!((bits >> key) & 1u)) s[rb][e] = -INFINITY;
+        if constexpr (MASKED) {
+          const int key = 8 * (e >> 2) + 4 * h + (e & 3);
+          if (!((key_bits[rb] >> key) & 1u)) s[rb][e] = -INFINITY;
+        }
         tmax = fmaxf(tmax, s[rb][e]);
       }
       tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-      const float mnew = fmaxf(m_run[rb], tmax);
-      const float muse = mnew == -INFINITY ? 0.f : mnew;
-      const float alpha = fast_exp2((m_run[rb] - muse) * c);
-      const float mc = muse * c;
+      const bool grow = (tmax - m_run[rb]) * c > 8.f;   // false when both are -inf (NaN)
+      if (__any(grow)) {
+        const float mnew = grow ? tmax : m_run[rb];
+        const float alpha = grow ? fast_exp2((m_run[rb] - mnew) * c) : 1.f;
+        l_run[rb] *= alpha;
+        m_run[rb] = mnew;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) o[rb][db][e] *= alpha;
+      }
+      const float mc = m_run[rb] == -INFINITY ? 0.f : m_run[rb] * c;
       float ls = 0.f;
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
@@ -311,16 +353,13 @@ void partial_kernel(PartialParams p) {
         s[rb][e] = pe;
         ls += pe;
       }
-      l_run[rb] = l_run[rb] * alpha + ls;
-      m_run[rb] = mnew;
-#pragma unroll
-      for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) o[rb][db][e] *= alpha;
+      l_run[rb] += ls;
     }
 
     // O^T += V_tile^T . P^T
-    if constexpr (ES == 2) {
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (BF) {
+      const int bk = lane >> 4, i16 = lane & 15;
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
         bf16x8 pb[RB];
@@ -330,12 +369,23 @@ void partial_kernel(PartialParams p) {
           for (int j = 0; j < 8; ++j) pb[rb][j] = (__bf16)s[rb][8 * ks + j];
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
-          // k-slots j = 0..3: keys 16ks + 4h + j; j = 4..7: keys 16ks + 8 + 4h + (j - 4)
-          const T* vrow = vt + (32 * db + n) * VT_LDR + 16 * ks + 4 * h;
-          typedef uint32_t u32x2 __attribute__((ext_vector_type(2), __may_alias__));
-          const u32x2 lo = *(const u32x2*)(vrow);
-          const u32x2 hi = *(const u32x2*)(vrow + 8);
-          const bf16x8 a = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+          __builtin_amdgcn_sched_barrier(0);
+          // Transposed LDS reads: this lane receives V[K0 + j][32db + n],
+          // j = 0..3, for K0 = 16ks + 4h (k-slots 0..3) and 16ks + 8 + 4h
+          // (k-slots 4..7), matching the key order of P^T's k-slots.
+          const int d = 32 * db + 16 * (bk & 1) + 4 * (i16 & 3);
+          uint32_t w[4];
+#pragma unroll
+          for (int rr = 0; rr < 2; ++rr) {
+            const int key = 16 * ks + 8 * rr + 4 * h + (i16 >> 2);
+            const T* src = vt + key * D + swz<CPR>(key, d >> 3) * VEC + (d & 7);
+            typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+            const i16x4 tv = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)src);
+            const u32x2 tw = __builtin_bit_cast(u32x2, tv);
+            w[2 * rr] = tw[0];
+            w[2 * rr + 1] = tw[1];
+          }
+          const bf16x8 a = __builtin_bit_cast(bf16x8, u32x4{w[0], w[1], w[2], w[3]});
 #pragma unroll
           for (int rb = 0; rb < RB; ++rb)
             o[rb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[rb], o[rb][db], 0, 0, 0);
@@ -347,11 +397,56 @@ void partial_kernel(PartialParams p) {
         const int key = 8 * (e >> 2) + 4 * h + (e & 3);
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
-          const float a = vt[(32 * db + n) * VT_LDR + key];
+          const int d = 32 * db + n;
+          const float a = vt[key * D + swz<CPR>(key, d / VEC) * VEC + d % VEC];
 #pragma unroll
           for (int rb = 0; rb < RB; ++rb)
             o[rb][db] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, s[rb][e], o[rb][db], 0, 0, 0);
         }
+      }
+    }
+  };
+
+  // ---- stream this wavefront's tiles.  The register copies of the next PF
+  // tiles form a ring: each 16-byte chunk is re-issued for the tile PF
+  // steps ahead as soon as it has been staged in LDS, so a wavefront keeps
+  // about PF tiles of loads in flight at all times.  Loads are never
+  // skipped (past the end a slot re-fetches a valid row that is never
+  // staged), so the wait before each staged chunk counts only older chunks.
+  uint32_t okbits[PF];
+  const int t0 = tfirst;
+#pragma unroll
+  for (int pp = 0; pp < PF; ++pp) {
+    okbits[pp] = 0;
+    const int tl = t0 + pp * tstep;
+    load_tile(tl < ntiles ? tl : (t0 < ntiles ? t0 : 0), kreg[pp], vreg[pp], vmask[pp], okbits[pp]);
+  }
+  for (int t = t0; t < ntiles; t += PF * tstep) {
+#pragma unroll
+    for (int pp = 0; pp < PF; ++pp) {
+      const int tp = t + pp * tstep;
+      if (tp >= ntiles) break;
+      const uint32_t vm = vmask[pp];
+      const int tn = tp + PF * tstep < ntiles ? tp + PF * tstep : tp;
+#pragma unroll
+      for (int cc = 0; cc < NCH; ++cc) {
+        const int chunk = lane + 64 * cc;
+        const int kk = chunk / CPR, col = chunk % CPR;
+        const int off = kk * D + swz<CPR>(kk, col) * VEC;
+        const bool ok = (okbits[pp] >> cc) & 1u;
+        const u32x4 z = u32x4{0, 0, 0, 0};
+        *(u32x4*)(kt + off) = ok ? kreg[pp][cc] : z;
+        *(u32x4*)(vt + off) = ok ? vreg[pp][cc] : z;
+        load_chunk(tn, cc, kreg[pp][cc], vreg[pp][cc], okbits[pp]);
+      }
+      vmask[pp] = tile_mask(tn);
+      if constexpr (KernelShape<RB, ES, D>::hbm_shape) {
+        if (!tree && vm == ~0u)
+          compute(tp, vm, std::false_type{});
+        else
+          compute(tp, vm, std::true_type{});
+      } else {
+        compute(tp, vm, std::true_type{});
       }
     }
   }
