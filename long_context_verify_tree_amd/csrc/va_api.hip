@@ -62,8 +62,10 @@ va::Plan make_plan(const va_attn_desc* d, int32_t n_ctx) {
   va::Plan pl{};
   const int G = d->Hq / d->Hkv;
   const int R = G * d->N;
-  pl.rb = R <= 32 ? 1 : 2;
-  const int rows_per_tile = 32 * pl.rb;
+  // bf16 with more than 64 query rows per KV head: the shared-tile rows
+  // kernel (256 rows per workgroup); otherwise 32 or 64 rows per workgroup.
+  pl.rb = (d->dtype == VA_BF16 && R > 64) ? va::kRowsKernel : (R <= 32 ? 1 : 2);
+  const int rows_per_tile = pl.rb == va::kRowsKernel ? 256 : 32 * pl.rb;
   pl.row_tiles = (R + rows_per_tile - 1) / rows_per_tile;
   const int64_t pairs = (int64_t)d->B * d->Hkv * pl.row_tiles;
   // Enough context workgroups to fill every CU slot, but no split shorter

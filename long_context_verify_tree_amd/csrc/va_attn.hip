@@ -66,6 +66,19 @@ __device__ inline int xcd_remap(int x, int total) {
 
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Workgroup barrier for LDS hand-offs inside the streaming loops.
+// __syncthreads() is a workgroup release/acquire fence and waits for every
+// outstanding global load too, which would drain the register prefetch ring
+// at each tile; this waits only for this wavefront's LDS operations
+// (lgkmcnt(0)) before the hardware barrier.  The empty asm statements keep
+// the compiler from moving memory accesses across it.
+__device__ inline void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // vmcnt(63) expcnt(7) lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // Bank-conflict swizzle of the 16-byte chunks of a key row in LDS.
 template <int CPR>
 __device__ inline int swz(int row, int chunk) {
@@ -132,7 +145,7 @@ void partial_kernel(PartialParams p) {
   const bool tree = part == p.n_ctx_splits;
   const int row0 = rt * 32 * RB;
 
-  auto q_row_ptr = [&](int r) -> const T* {
+  auto q_row_ptr = [&](int r) __attribute__((always_inline)) -> const T* {
     const int g = r / p.N, i = r % p.N;
     return (const T*)p.q + (int64_t)b * p.qs[0] + (int64_t)(kvh * p.G + g) * p.qs[1] + (int64_t)i * p.qs[2];
   };
@@ -222,7 +235,7 @@ void partial_kernel(PartialParams p) {
   // issued for every lane (invalid ones read row 0, which always exists when
   // a part has keys) and zeroed afterwards, so the load stream has no
   // branches and the wait counts before each staged chunk stay partial.
-  auto key_pos = [&](int key, bool& ok) -> int64_t {
+  auto key_pos = [&](int key, bool& ok) __attribute__((always_inline)) -> int64_t {
     ok = key < ke;
     int64_t pos = ok ? key : 0;
     if constexpr (GATHER) {
@@ -239,7 +252,7 @@ void partial_kernel(PartialParams p) {
   // The raw chunk stays in registers; whether it holds a real key is kept
   // as bit c of `okbits` and applied when the chunk is staged, so nothing
   // waits on the load before then.
-  auto load_chunk = [&](int t, int c, u32x4& kr, u32x4& vr, uint32_t& okbits) {
+  auto load_chunk = [&](int t, int c, u32x4& kr, u32x4& vr, uint32_t& okbits) __attribute__((always_inline)) {
     const int chunk = lane + 64 * c;
     const int kk = chunk / CPR, col = chunk % CPR;
     bool ok;
@@ -248,12 +261,12 @@ void partial_kernel(PartialParams p) {
     vr = *(const u32x4*)(vbase + pos * vts + col * VEC);
     okbits = (okbits & ~(1u << c)) | ((uint32_t)ok << c);
   };
-  auto tile_mask = [&](int t) -> uint32_t {
+  auto tile_mask = [&](int t) __attribute__((always_inline)) -> uint32_t {
     bool mine;
     key_pos(kb + kTileKeys * t + n, mine);
     return (uint32_t)__ballot(mine && h == 0);
   };
-  auto load_tile = [&](int t, u32x4 (&kr)[NCH], u32x4 (&vr)[NCH], uint32_t& vm, uint32_t& okbits) {
+  auto load_tile = [&](int t, u32x4 (&kr)[NCH], u32x4 (&vr)[NCH], uint32_t& vm, uint32_t& okbits) __attribute__((always_inline)) {
 #pragma unroll
     for (int c = 0; c < NCH; ++c) load_chunk(t, c, kr[c], vr[c], okbits);
     vm = tile_mask(t);
@@ -277,7 +290,7 @@ void partial_kernel(PartialParams p) {
   // invisible keys (the last context tile, the tree part); whole context
   // tiles take the unmasked instance.  The choice is made before the MFMAs,
   // so no branch separates the S^T chain from the reads of its accumulators.
-  auto compute = [&](int t, uint32_t vm, auto masked_tag) {
+  auto compute = [&](int t, uint32_t vm, auto masked_tag) __attribute__((always_inline)) {
     constexpr bool MASKED = decltype(masked_tag)::value;
     uint32_t key_bits[RB];
 #pragma unroll
@@ -519,6 +532,291 @@ void partial_kernel(PartialParams p) {
   }
 }
 
+// Many query rows per KV head (a large draft tree times the GQA group).
+// Eight wavefronts own 32 query rows each (256 rows per workgroup) and share
+// every 32-key K/V tile through a two-stage LDS buffer, so K/V bytes are
+// read once per 256 rows.  Two wavefronts per SIMD let one wavefront's
+// softmax overlap the other's MFMAs.  The workgroup's threads keep a ring of
+// RING tiles of 16-byte chunks in flight in registers; one LDS barrier per
+// tile.  Every wavefront sees every key of the part, so its rows' partials
+// are written directly.
+constexpr int kRowsWaves = 8;
+constexpr int kRowsThreads = 64 * kRowsWaves;
+
+template <int D, bool GATHER>
+__global__ __launch_bounds__(kRowsThreads) __attribute__((amdgpu_waves_per_eu(2)))
+void rows_kernel(PartialParams p) {
+  using T = uint16_t;
+  constexpr int VEC = 8;
+  constexpr int CPR = D / VEC;
+  constexpr int GROWS = 32 * kRowsWaves;             // rows per workgroup
+  constexpr int TILE_ELEMS = kTileKeys * D;
+  constexpr int STAGE_ELEMS = 2 * TILE_ELEMS;        // K tile then V tile
+  constexpr int KCH = kTileKeys * CPR;               // chunks of one K (or V) tile
+  constexpr int NCT = 2 * KCH / kRowsThreads;        // K+V chunks per thread per tile
+  constexpr int RING = D == 128 ? 6 : 8;
+  constexpr int NDB = D / 32;
+  static_assert(NCT >= 1 && NCT * kRowsThreads == 2 * KCH, "tile must split evenly over the workgroup");
+
+  __shared__ __attribute__((aligned(16))) T stage[2 * STAGE_ELEMS];
+  __shared__ uint32_t anc[GROWS][kAncWords];
+  __shared__ int par[kMaxN];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int h = lane >> 5;
+  const int n = lane & 31;
+
+  int id = xcd_remap(blockIdx.x, p.total_groups);
+  const int rt = id % p.row_tiles;
+  id /= p.row_tiles;
+  const int part = id % p.n_parts;
+  id /= p.n_parts;
+  const int kvh = id % p.Hkv;
+  const int b = id / p.Hkv;
+  const bool tree = part == p.n_ctx_splits;
+  const int row0 = rt * GROWS;
+
+  if (tree) {
+    for (int j = tid; j < p.N; j += kRowsThreads) par[j] = p.parent[(int64_t)b * p.N + j];
+    for (int j = tid; j < GROWS * kAncWords; j += kRowsThreads) (&anc[0][0])[j] = 0u;
+    __syncthreads();
+    if (tid < GROWS && row0 + tid < p.R) {
+      int j = (row0 + tid) % p.N;
+      for (int step = 0; step <= p.N && j >= 0; ++step) {
+        anc[tid][j >> 5] |= 1u << (j & 31);
+        int pj = par[j];
+        j = (pj >= -1 && pj < j) ? pj : -1;  // malformed parents end the path
+      }
+    }
+  } else {
+    for (int j = tid; j < GROWS * kAncWords; j += kRowsThreads) (&anc[0][0])[j] = ~0u;
+  }
+  __syncthreads();
+
+  // queries of this wavefront's 32 rows as MFMA B operands (Q^T)
+  const int myrow = row0 + 32 * wave + n;
+  bf16x8 qop[D / 16];
+  {
+    const bool ok = myrow < p.R;
+    const int g = ok ? myrow / p.N : 0, i = ok ? myrow % p.N : 0;
+    const T* qrow = (const T*)p.q + (int64_t)b * p.qs[0] + (int64_t)(kvh * p.G + g) * p.qs[1] + (int64_t)i * p.qs[2];
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      const u32x4 v = ok ? *(const u32x4*)(qrow + 16 * ks + 8 * h) : u32x4{0, 0, 0, 0};
+      qop[ks] = __builtin_bit_cast(bf16x8, v);
+    }
+  }
+
+  const T* kbase;
+  const T* vbase;
+  int64_t kts, vts;
+  int kb, ke;
+  if (tree) {
+    kbase = (const T*)p.kd + (int64_t)b * p.kds[0] + (int64_t)kvh * p.kds[1];
+    vbase = (const T*)p.vd + (int64_t)b * p.vds[0] + (int64_t)kvh * p.vds[1];
+    kts = p.kds[2];
+    vts = p.vds[2];
+    kb = 0;
+    ke = p.N;
+  } else {
+    kbase = (const T*)p.kc + (int64_t)b * p.kcs[0] + (int64_t)kvh * p.kcs[1];
+    vbase = (const T*)p.vc + (int64_t)b * p.vcs[0] + (int64_t)kvh * p.vcs[1];
+    kts = p.kcs[2];
+    vts = p.vcs[2];
+    kb = part * p.split_len;
+    ke = min(p.n_ctx, kb + p.split_len);
+  }
+  const bool gather = GATHER && !tree;
+  const int32_t* idx_row = GATHER ? p.idx + (int64_t)b * p.idx_stride : nullptr;
+  const int ntiles = ke > kb ? (ke - kb + kTileKeys - 1) / kTileKeys : 0;
+
+  auto key_pos = [&](int key, bool& ok) __attribute__((always_inline)) -> int64_t {
+    ok = key < ke;
+    int64_t pos = ok ? key : kb;
+    if constexpr (GATHER) {
+      if (gather) {
+        const int ix = idx_row[ok ? key : kb];
+        ok = ok && (unsigned)ix < (unsigned)p.L;
+        pos = ok ? ix : 0;
+      }
+    }
+    return pos;
+  };
+
+  // Thread chunk j of a tile: combined index tid + 512 j; the first KCH are
+  // K chunks, the rest V chunks; chunk -> (key row, 16-byte column).
+  u32x4 rg[RING][NCT];
+  uint32_t okb[RING], vmk[RING];
+  auto load = [&](int t, u32x4 (&rx)[NCT], uint32_t& ok_bits, uint32_t& vm) __attribute__((always_inline)) {
+    const int tc = t < ntiles ? t : (ntiles > 0 ? ntiles - 1 : 0);   // past the end: refetch, never staged
+    ok_bits = 0;
+#pragma unroll
+    for (int j = 0; j < NCT; ++j) {
+      const int ci = tid + kRowsThreads * j;
+      const bool isv = ci >= KCH;
+      const int ch = isv ? ci - KCH : ci;
+      const int kk = ch / CPR, col = ch % CPR;
+      bool ok;
+      const int64_t pos = key_pos(kb + kTileKeys * tc + kk, ok);
+      const T* src = isv ? vbase + pos * vts : kbase + pos * kts;
+      rx[j] = *(const u32x4*)(src + col * VEC);
+      ok_bits |= (uint32_t)ok << j;
+    }
+    bool mine;
+    key_pos(kb + kTileKeys * tc + n, mine);
+    vm = (uint32_t)__ballot(mine && h == 0);
+  };
+  auto stage_write = [&](const u32x4 (&rx)[NCT], uint32_t ok_bits, int buf) __attribute__((always_inline)) {
+    T* base = stage + buf * STAGE_ELEMS;
+#pragma unroll
+    for (int j = 0; j < NCT; ++j) {
+      const int ci = tid + kRowsThreads * j;
+      const bool isv = ci >= KCH;
+      const int ch = isv ? ci - KCH : ci;
+      const int kk = ch / CPR, col = ch % CPR;
+      const int off = (isv ? TILE_ELEMS : 0) + kk * D + swz<CPR>(kk, col) * VEC;
+      const bool ok = (ok_bits >> j) & 1u;
+      *(u32x4*)(base + off) = ok ? rx[j] : u32x4{0, 0, 0, 0};
+    }
+  };
+
+  float m_run = -INFINITY, l_run = 0.f;
+  f32x16 o[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) o[db][e] = 0.f;
+  const float c = p.c;
+
+  auto compute = [&](int t, int buf, uint32_t vm, auto masked_tag) __attribute__((always_inline)) {
+    constexpr bool MASKED = decltype(masked_tag)::value;
+    const T* kt = stage + buf * STAGE_ELEMS;
+    const T* vt = kt + TILE_ELEMS;
+    const uint32_t key_bits = MASKED ? vm & anc[32 * wave + n][t & (kAncWords - 1)] : ~0u;
+
+    f32x16 s;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) s[e] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      const u32x4 kv = *(const u32x4*)(kt + n * D + swz<CPR>(n, 2 * ks + h) * VEC);
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kv), qop[ks], s, 0, 0, 0);
+    }
+
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      if constexpr (MASKED) {
+        const int key = 8 * (e >> 2) + 4 * h + (e & 3);
+        if (!((key_bits >> key) & 1u)) s[e] = -INFINITY;
+      }
+      tmax = fmaxf(tmax, s[e]);
+    }
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+    const bool grow = (tmax - m_run) * c > 8.f;
+    if (__any(grow)) {
+      const float mnew = grow ? tmax : m_run;
+      const float alpha = grow ? fast_exp2((m_run - mnew) * c) : 1.f;
+      l_run *= alpha;
+      m_run = mnew;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) o[db][e] *= alpha;
+    }
+    const float mc = m_run == -INFINITY ? 0.f : m_run * c;
+    float ls = 0.f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const float pe = fast_exp2(fmaf(s[e], c, -mc));
+      s[e] = pe;
+      ls += pe;
+    }
+    l_run += ls;
+
+    const int bk = lane >> 4, i16 = lane & 15;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      bf16x8 pb;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) pb[j] = (__bf16)s[8 * ks + j];
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const int d = 32 * db + 16 * (bk & 1) + 4 * (i16 & 3);
+        uint32_t w[4];
+#pragma unroll
+        for (int rr = 0; rr < 2; ++rr) {
+          const int key = 16 * ks + 8 * rr + 4 * h + (i16 >> 2);
+          const T* src = vt + key * D + swz<CPR>(key, d >> 3) * VEC + (d & 7);
+          typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+          const i16x4 tv = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)src);
+          const u32x2 tw = __builtin_bit_cast(u32x2, tv);
+          w[2 * rr] = tw[0];
+          w[2 * rr + 1] = tw[1];
+        }
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, u32x4{w[0], w[1], w[2], w[3]}),
+                                                         pb, o[db], 0, 0, 0);
+      }
+    }
+  };
+
+  // prologue: tiles 0..RING-1 in flight, tile 0 staged
+#pragma unroll
+  for (int pp = 0; pp < RING; ++pp) load(pp, rg[pp], okb[pp], vmk[pp]);
+  stage_write(rg[0], okb[0], 0);
+  uint32_t vm_cur = vmk[0];
+  load(RING, rg[0], okb[0], vmk[0]);
+  lds_barrier();
+
+  // Tiles [0, t_end): compute tile t from LDS buffer t & 1, then stage tile
+  // t+1 from its ring slot and refill the slot with tile t+1+RING.  Each
+  // call site has one compute variant, so no loop body holds both.
+  auto tile_loop = [&](int t_end, auto masked_tag) __attribute__((always_inline)) {
+    for (int t0 = 0; t0 < t_end; t0 += RING) {
+#pragma unroll
+      for (int pp = 0; pp < RING; ++pp) {
+        const int t = t0 + pp;
+        if (t >= t_end) break;
+        compute(t, t & 1, vm_cur, masked_tag);
+        const int nx = (pp + 1) % RING;
+        stage_write(rg[nx], okb[nx], (t + 1) & 1);
+        vm_cur = vmk[nx];
+        load(t + 1 + RING, rg[nx], okb[nx], vmk[nx]);
+        lds_barrier();
+      }
+    }
+  };
+  if (tree) {
+    tile_loop(ntiles, std::true_type{});
+  } else {
+    // whole tiles without the mask, then the partial tail tile (already
+    // staged in buffer nfull & 1 by the loop) with it
+    const int nfull = (ke - kb) / kTileKeys;
+    tile_loop(nfull, std::false_type{});
+    if (nfull < ntiles) compute(nfull, nfull & 1, vm_cur, std::true_type{});
+  }
+
+  // this wavefront's rows: normalised partial and log2-sum-exp
+  const float l = l_run + __shfl_xor(l_run, 32);
+  if (myrow < p.R) {
+    const int g = myrow / p.N, i = myrow % p.N;
+    const int64_t prow = ((int64_t)b * p.Hq + kvh * p.G + g) * p.N + i;
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    float* dst = p.part_o + (prow * p.n_parts + part) * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        float4 v = make_float4(o[db][4 * q4] * inv, o[db][4 * q4 + 1] * inv, o[db][4 * q4 + 2] * inv,
+                               o[db][4 * q4 + 3] * inv);
+        *(float4*)(dst + 32 * db + 8 * q4 + 4 * h) = v;
+      }
+    if (h == 0) p.part_lse[prow * p.n_parts + part] = l > 0.f ? m_run * c + log2f(l) : -INFINITY;
+  }
+}
+
 template <class T, int D>
 __global__ __launch_bounds__(256) void merge_kernel(MergeParams p) {
   // One wavefront per output row.  Lane s holds part s's log2-sum-exp; the
@@ -600,10 +898,20 @@ hipError_t launch_p_rb(const PartialParams& p, int rb, bool gather, hipStream_t 
   return gather ? launch_p<T, D, 2, true>(p, stream) : launch_p<T, D, 2, false>(p, stream);
 }
 
+template <int D, bool G>
+hipError_t launch_rows(const PartialParams& p, hipStream_t stream) {
+  hipLaunchKernelGGL((rows_kernel<D, G>), dim3(p.total_groups), dim3(kRowsThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_partials(const PartialParams& p, int dtype, int D, int rb, bool gather,
                            hipStream_t stream) {
+  if (rb == kRowsKernel) {
+    if (D == 64) return gather ? launch_rows<64, true>(p, stream) : launch_rows<64, false>(p, stream);
+    return gather ? launch_rows<128, true>(p, stream) : launch_rows<128, false>(p, stream);
+  }
   if (dtype == 1) {
     return D == 64 ? launch_p_rb<uint16_t, 64>(p, rb, gather, stream)
                    : launch_p_rb<uint16_t, 128>(p, rb, gather, stream);

@@ -17,8 +17,12 @@ namespace va {
 // split_len keys; the draft (tree) keys form one more part.  Every
 // (sequence, kv head, row tile, part) is one workgroup that writes one
 // normalised partial output and its log2-sum-exp.
+// Plan::rb value selecting rows_kernel (bf16, many query rows per KV head:
+// 256 rows per workgroup, 64 per wavefront, K/V tiles shared in LDS).
+constexpr int kRowsKernel = 8;
+
 struct Plan {
-  int rb;            // 32-row blocks per wave (1 or 2)
+  int rb;            // 32-row blocks per wave (1 or 2), or kRowsKernel
   int row_tiles;     // ceil(G * N / (32 * rb))
   int split_len;     // context keys per split (multiple of 128)
   int n_ctx_splits;  // ceil(n_ctx / split_len); 0 when n_ctx == 0
