@@ -50,14 +50,15 @@ def algorithmic(cfg, n_ctx: int, sparse: bool):
                 flops=flops)
 
 
-KERNEL_SOURCE = os.path.join(ROOT, "long_context_verify_tree_amd", "csrc", "va_attn.hip")
+CSRC = os.path.join(ROOT, "long_context_verify_tree_amd", "csrc")
+KERNEL_SOURCES = {"partial_kernel": "va_attn.hip", "rows_kernel": "va_attn.hip", "select_kernel": "va_select.hip"}
 
 
-def committed_traffic(workload: str):
-    """HBM bytes per partial-kernel launch from the committed rocprofv3 counter
+def committed_traffic(kernel: str, workload: str):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
     summary, or None if there is none or the kernel source changed since."""
     import hashlib
-    path = os.path.join(ROOT, "profiles", f"partial_kernel_{workload}.md")
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}.md")
     if not os.path.exists(path):
         return None, None
     fields = {}
@@ -65,10 +66,55 @@ def committed_traffic(workload: str):
         if ":" in line and line.startswith("- "):
             k, v = line[2:].split(":", 1)
             fields[k.strip()] = v.strip().strip("`")
-    digest = hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()
+    digest = hashlib.sha256(open(os.path.join(CSRC, KERNEL_SOURCES[kernel]), "rb").read()).hexdigest()
     if fields.get("kernel source sha256") != digest or "traffic bytes per launch" not in fields:
         return None, os.path.relpath(path, ROOT) + " (stale: kernel changed since the counters were taken)"
     return int(float(fields["traffic bytes per launch"])), os.path.relpath(path, ROOT)
+
+
+def attention_kernel(cfg) -> str:
+    """Which partial kernel the library picks: the shared-tile kernel for bf16
+    with more than 64 query rows per KV head, the per-wavefront kernel else."""
+    return "rows_kernel" if cfg.dtype == "bf16" and cfg.G * cfg.N > 64 else "partial_kernel"
+
+
+def measured_read_peak(torch, dev, gib: float = 2.0, reps: int = 10, min_seconds: float = 0.4):
+    """Achievable HBM read bandwidth (GB/s) from the read-only probe library.
+    Also keeps the GPU busy for at least `min_seconds` first, so the timed
+    steps that follow run at a settled clock."""
+    import ctypes
+    path = os.path.join(ROOT, "long_context_verify_tree_amd", "libva_probe.so")
+    if not os.path.exists(path):
+        return None
+    lib = ctypes.CDLL(path)
+    lib.va_probe_hbm_read.restype = ctypes.c_int
+    lib.va_probe_hbm_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int,
+                                      ctypes.c_void_p]
+    n = int(gib * (1 << 30))
+    buf = torch.ones(n // 4, dtype=torch.int32, device=dev)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream().cuda_stream
+    t_end = time.perf_counter() + min_seconds
+    while time.perf_counter() < t_end:
+        for _ in range(20):
+            lib.va_probe_hbm_read(buf.data_ptr(), n, sink.data_ptr(), 256 * 16, stream)
+        torch.cuda.synchronize()
+    best = 0.0
+    for grid in (256 * 8, 256 * 16, 256 * 32):
+        def run():
+            rc = lib.va_probe_hbm_read(buf.data_ptr(), n, sink.data_ptr(), grid, stream)
+            if rc != 0:
+                raise RuntimeError(f"va_probe_hbm_read failed: {rc}")
+        run()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            run()
+        b.record()
+        b.synchronize()
+        best = max(best, reps * n / (a.elapsed_time(b) * 1e-3) / 1e9)
+    del buf
+    return round(best, 1)
 
 
 def cpu_baseline(cfg, x, budget_s: float):
@@ -109,7 +155,7 @@ def cpu_baseline(cfg, x, budget_s: float):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default=DEFAULT_CONFIG)
     ap.add_argument("--copies", type=int, default=0, help="input copies rotated over steps (0: auto)")
@@ -175,16 +221,26 @@ def main():
         if ev is not None:
             ev[3].record()
 
+    # achievable read bandwidth; this also brings the clock up before warm-up
+    read_peak = measured_read_peak(torch, dev)
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
+    # timed region: exactly K whole steps, nothing else on the stream
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(args.warmup + i, evs[i])
+        step(args.warmup + i)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    # the same K steps again with HIP events on the launching stream around
+    # each stage, for the per-kernel durations the roofline uses
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + args.steps + i, evs[i])
+    torch.cuda.synchronize()
+    wall_ev = time.perf_counter() - t1
 
     sel_ms = [e[0].elapsed_time(e[1]) for e in evs]
     part_ms = [e[1].elapsed_time(e[2]) for e in evs]
@@ -192,20 +248,41 @@ def main():
     ms_per_step = wall * 1e3 / args.steps
     a = algorithmic(cfg, n_ctx, sparse)
     value = a["step_bytes"] / (ms_per_step * 1e-3) / 1e9
+
+    def pct(xs, q):
+        return round(float(np.percentile(xs, q)), 4)
+
     part_avg = statistics.mean(part_ms)
-    achieved = a["partial_bytes"] / (part_avg * 1e-3) / 1e9
-    flops_rate = a["flops"] / (part_avg * 1e-3) / 1e12
-    mfma_bound = a["flops"] / a["partial_bytes"] > (MFMA_BF16_PEAK_TFLOPS * 1e12) / (HBM_PEAK_GBS * 1e9)
-    if mfma_bound:
-        roof = {"bound": "mfma", "achieved": round(flops_rate, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(flops_rate / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None}
+    sel_avg = statistics.mean(sel_ms) if sparse else 0.0
+    if sparse and sel_avg > part_avg:
+        # the selector dominates: an HBM scan of both score rows plus the index write
+        kernel = "select_kernel"
+        sel_bytes = 2 * cfg.B * cfg.L * 4 + cfg.B * n_ctx * 4
+        ach = sel_bytes / (sel_avg * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None}
+        roof["kernel_avg_us"] = round(sel_avg * 1e3, 2)
+        roof["algorithmic_bytes_per_launch"] = sel_bytes
     else:
-        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None}
-    roof["kernel"] = "partial_kernel"
-    roof["kernel_avg_us"] = round(part_avg * 1e3, 2)
-    roof["algorithmic_bytes_per_launch"] = a["partial_bytes"]
-    roof["algorithmic_flops_per_launch"] = a["flops"]
+        kernel = attention_kernel(cfg)
+        achieved = a["partial_bytes"] / (part_avg * 1e-3) / 1e9
+        flops_rate = a["flops"] / (part_avg * 1e-3) / 1e12
+        mfma_bound = a["flops"] / a["partial_bytes"] > (MFMA_BF16_PEAK_TFLOPS * 1e12) / (HBM_PEAK_GBS * 1e9)
+        if mfma_bound:
+            roof = {"bound": "mfma", "achieved": round(flops_rate, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(flops_rate / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None}
+        else:
+            roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None}
+        roof["kernel_avg_us"] = round(part_avg * 1e3, 2)
+        roof["kernel_p10_p90_us"] = [round(pct(part_ms, 10) * 1e3, 2), round(pct(part_ms, 90) * 1e3, 2)]
+        roof["algorithmic_bytes_per_launch"] = a["partial_bytes"]
+        roof["algorithmic_flops_per_launch"] = a["flops"]
+        roof["hbm_gbs"] = round(achieved, 1)
+        if read_peak:
+            roof["frac_of_measured_read_peak"] = round(achieved / read_peak, 4)
+    roof["kernel"] = kernel
+    roof["measured_read_peak_gbs"] = read_peak
 
     line = {
         "metric": "verify-attention HBM GB/s (% of peak) + draft tokens verified/sec per layer",
@@ -217,8 +294,11 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 4),
-        "stage_ms": {"select": round(statistics.median(sel_ms), 4), "partials": round(statistics.median(part_ms), 4),
-                     "merge": round(statistics.median(merge_ms), 4)},
+        "stage_ms": {"select": round(statistics.median(sel_ms), 4) if sparse else 0.0,
+                     "partials": round(statistics.median(part_ms), 4),
+                     "merge": round(statistics.median(merge_ms), 4),
+                     "partials_p10_p90": [pct(part_ms, 10), pct(part_ms, 90)],
+                     "instrumented_step": round(wall_ev * 1e3 / args.steps, 4)},
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -229,7 +309,7 @@ def main():
                    "verify": "sparse" if sparse else "dense", "n_ctx_keys": n_ctx},
         "roofline": roof,
     }
-    roof["traffic"], roof["traffic_source"] = committed_traffic(cfg.name)
+    roof["traffic"], roof["traffic_source"] = committed_traffic(kernel, cfg.name)
     if args.copy_calib_gib > 0:
         n = int(args.copy_calib_gib * (1 << 30))
         src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)

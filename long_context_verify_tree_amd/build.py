@@ -15,6 +15,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libverify_attn.so")
+PROBE_SRC = os.path.join(PKG, "probe", "hbm_read.hip")
+PROBE_LIB = os.path.join(PKG, "libva_probe.so")
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",
@@ -42,10 +44,9 @@ def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every HIP source into one shared library; returns its path."""
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"), *sources(), "-o", tmp]
+def _compile(srcs, out: str, verbose: bool) -> str:
+    tmp = out + ".tmp"
+    cmd = [hipcc(), *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"), *srcs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -55,7 +56,15 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
     if verbose and err.strip():
         print(err, file=sys.stderr)
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
+    return out
+
+
+def build(verbose: bool = False) -> str:
+    """Compile the verification library (every csrc/*.hip) and the HBM read
+    probe library; returns the verification library's path."""
+    _compile(sources(), LIB, verbose)
+    _compile([PROBE_SRC], PROBE_LIB, verbose)
     return LIB
 
 

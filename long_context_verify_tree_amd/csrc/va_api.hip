@@ -68,11 +68,12 @@ va::Plan make_plan(const va_attn_desc* d, int32_t n_ctx) {
   const int rows_per_tile = pl.rb == va::kRowsKernel ? 256 : 32 * pl.rb;
   pl.row_tiles = (R + rows_per_tile - 1) / rows_per_tile;
   const int64_t pairs = (int64_t)d->B * d->Hkv * pl.row_tiles;
-  // Enough context workgroups to fill every CU slot, but no split shorter
-  // than 512 keys: every split costs one partial row per query row in the
-  // workspace.
+  // About one context workgroup per CU (the partial kernels run one
+  // workgroup per CU), i.e. a single round with no second wave of
+  // workgroups starting late, but no split shorter than 512 keys: every
+  // split costs one partial row per query row in the workspace.
 #ifndef VA_TARGET_GROUPS
-#define VA_TARGET_GROUPS 512
+#define VA_TARGET_GROUPS 256
 #endif
   const int64_t target_groups = VA_TARGET_GROUPS;
   int64_t want_splits = (target_groups + pairs - 1) / pairs;

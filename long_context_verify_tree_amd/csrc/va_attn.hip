@@ -79,6 +79,40 @@ __device__ inline void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
+#ifndef VA_TREE_FIRST
+#define VA_TREE_FIRST 1
+#endif
+// Work item of this workgroup: (row tile, part, kv head, sequence).
+// The draft-tree parts are short; with VA_TREE_FIRST they take the lowest
+// workgroup ids, which are dispatched first, so no long context part waits
+// behind them.  Context parts are mapped XCD-aware among themselves.
+__device__ inline void decode_group(const PartialParams& p, int& rt, int& part, int& kvh, int& b) {
+  int id;
+  if (VA_TREE_FIRST) {
+    const int ntree = p.B * p.Hkv * p.row_tiles;
+    if ((int)blockIdx.x < ntree) {
+      id = blockIdx.x;
+      rt = id % p.row_tiles;
+      id /= p.row_tiles;
+      part = p.n_ctx_splits;
+    } else {
+      id = xcd_remap(blockIdx.x - ntree, p.total_groups - ntree);
+      rt = id % p.row_tiles;
+      id /= p.row_tiles;
+      part = id % p.n_ctx_splits;
+      id /= p.n_ctx_splits;
+    }
+  } else {
+    id = xcd_remap(blockIdx.x, p.total_groups);
+    rt = id % p.row_tiles;
+    id /= p.row_tiles;
+    part = id % p.n_parts;
+    id /= p.n_parts;
+  }
+  kvh = id % p.Hkv;
+  b = id / p.Hkv;
+}
+
 // Bank-conflict swizzle of the 16-byte chunks of a key row in LDS.
 template <int CPR>
 __device__ inline int swz(int row, int chunk) {
@@ -135,13 +169,8 @@ void partial_kernel(PartialParams p) {
   const int n = lane & 31;     // row (B / C column) owned by this lane
 
   // ---- which work item
-  int id = xcd_remap(blockIdx.x, p.total_groups);
-  const int rt = id % p.row_tiles;
-  id /= p.row_tiles;
-  const int part = id % p.n_parts;
-  id /= p.n_parts;
-  const int kvh = id % p.Hkv;
-  const int b = id / p.Hkv;
+  int rt, part, kvh, b;
+  decode_group(p, rt, part, kvh, b);
   const bool tree = part == p.n_ctx_splits;
   const int row0 = rt * 32 * RB;
 
@@ -424,43 +453,58 @@ void partial_kernel(PartialParams p) {
   // tiles form a ring: each 16-byte chunk is re-issued for the tile PF
   // steps ahead as soon as it has been staged in LDS, so a wavefront keeps
   // about PF tiles of loads in flight at all times.  Loads are never
-  // skipped (past the end a slot re-fetches a valid row that is never
-  // staged), so the wait before each staged chunk counts only older chunks.
+  // skipped (past the end a slot re-fetches this wavefront's last tile,
+  // which is never staged), and the main loop body takes every ring slot
+  // with no early exit, so the wait before each staged chunk counts only
+  // that slot's older chunks; the last (fewer than PF) tiles are drained
+  // after it.
+  const int nw = tfirst < ntiles ? (ntiles - 1 - tfirst) / tstep + 1 : 0;   // tiles of this wavefront
+  const int klast = nw > 0 ? nw - 1 : 0;
   uint32_t okbits[PF];
-  const int t0 = tfirst;
 #pragma unroll
   for (int pp = 0; pp < PF; ++pp) {
     okbits[pp] = 0;
-    const int tl = t0 + pp * tstep;
-    load_tile(tl < ntiles ? tl : (t0 < ntiles ? t0 : 0), kreg[pp], vreg[pp], vmask[pp], okbits[pp]);
+    load_tile(tfirst + (pp < klast ? pp : klast) * tstep, kreg[pp], vreg[pp], vmask[pp], okbits[pp]);
   }
-  for (int t = t0; t < ntiles; t += PF * tstep) {
+  auto stage = [&](int pp, bool reload, int tn) __attribute__((always_inline)) {
+#pragma unroll
+    for (int cc = 0; cc < NCH; ++cc) {
+      const int chunk = lane + 64 * cc;
+      const int kk = chunk / CPR, col = chunk % CPR;
+      const int off = kk * D + swz<CPR>(kk, col) * VEC;
+      const bool ok = (okbits[pp] >> cc) & 1u;
+      const u32x4 z = u32x4{0, 0, 0, 0};
+      *(u32x4*)(kt + off) = ok ? kreg[pp][cc] : z;
+      *(u32x4*)(vt + off) = ok ? vreg[pp][cc] : z;
+      if (reload) load_chunk(tn, cc, kreg[pp][cc], vreg[pp][cc], okbits[pp]);
+    }
+  };
+  auto run_tile = [&](int tp, uint32_t vm) __attribute__((always_inline)) {
+    if constexpr (KernelShape<RB, ES, D>::hbm_shape) {
+      if (!tree && vm == ~0u)
+        compute(tp, vm, std::false_type{});
+      else
+        compute(tp, vm, std::true_type{});
+    } else {
+      compute(tp, vm, std::true_type{});
+    }
+  };
+  int k = 0;
+  for (; k + PF <= nw; k += PF) {
 #pragma unroll
     for (int pp = 0; pp < PF; ++pp) {
-      const int tp = t + pp * tstep;
-      if (tp >= ntiles) break;
       const uint32_t vm = vmask[pp];
-      const int tn = tp + PF * tstep < ntiles ? tp + PF * tstep : tp;
+      const int kn = k + pp + PF < klast ? k + pp + PF : klast;
+      stage(pp, true, tfirst + kn * tstep);
+      vmask[pp] = tile_mask(tfirst + kn * tstep);
+      run_tile(tfirst + (k + pp) * tstep, vm);
+    }
+  }
 #pragma unroll
-      for (int cc = 0; cc < NCH; ++cc) {
-        const int chunk = lane + 64 * cc;
-        const int kk = chunk / CPR, col = chunk % CPR;
-        const int off = kk * D + swz<CPR>(kk, col) * VEC;
-        const bool ok = (okbits[pp] >> cc) & 1u;
-        const u32x4 z = u32x4{0, 0, 0, 0};
-        *(u32x4*)(kt + off) = ok ? kreg[pp][cc] : z;
-        *(u32x4*)(vt + off) = ok ? vreg[pp][cc] : z;
-        load_chunk(tn, cc, kreg[pp][cc], vreg[pp][cc], okbits[pp]);
-      }
-      vmask[pp] = tile_mask(tn);
-      if constexpr (KernelShape<RB, ES, D>::hbm_shape) {
-        if (!tree && vm == ~0u)
-          compute(tp, vm, std::false_type{});
-        else
-          compute(tp, vm, std::true_type{});
-      } else {
-        compute(tp, vm, std::true_type{});
-      }
+  for (int pp = 0; pp < PF - 1; ++pp) {
+    if (k + pp < nw) {
+      stage(pp, false, 0);
+      run_tile(tfirst + (k + pp) * tstep, vmask[pp]);
     }
   }
 
@@ -568,13 +612,8 @@ void rows_kernel(PartialParams p) {
   const int h = lane >> 5;
   const int n = lane & 31;
 
-  int id = xcd_remap(blockIdx.x, p.total_groups);
-  const int rt = id % p.row_tiles;
-  id /= p.row_tiles;
-  const int part = id % p.n_parts;
-  id /= p.n_parts;
-  const int kvh = id % p.Hkv;
-  const int b = id / p.Hkv;
+  int rt, part, kvh, b;
+  decode_group(p, rt, part, kvh, b);
   const bool tree = part == p.n_ctx_splits;
   const int row0 = rt * GROWS;
 
@@ -772,18 +811,32 @@ void rows_kernel(PartialParams p) {
 
   // Tiles [0, t_end): compute tile t from LDS buffer t & 1, then stage tile
   // t+1 from its ring slot and refill the slot with tile t+1+RING.  Each
-  // call site has one compute variant, so no loop body holds both.
+  // call site has one compute variant, so no loop body holds both.  The main
+  // loop takes whole turns of the ring with no early exit, which keeps the
+  // compiler's wait before each staged slot partial; the last turn (fewer
+  // than RING tiles, nothing left to load) follows it.
   auto tile_loop = [&](int t_end, auto masked_tag) __attribute__((always_inline)) {
-    for (int t0 = 0; t0 < t_end; t0 += RING) {
+    int t0 = 0;
+    for (; t0 + RING <= t_end; t0 += RING) {
 #pragma unroll
       for (int pp = 0; pp < RING; ++pp) {
         const int t = t0 + pp;
-        if (t >= t_end) break;
         compute(t, t & 1, vm_cur, masked_tag);
         const int nx = (pp + 1) % RING;
         stage_write(rg[nx], okb[nx], (t + 1) & 1);
         vm_cur = vmk[nx];
         load(t + 1 + RING, rg[nx], okb[nx], vmk[nx]);
+        lds_barrier();
+      }
+    }
+#pragma unroll
+    for (int pp = 0; pp < RING - 1; ++pp) {
+      const int t = t0 + pp;
+      if (t < t_end) {
+        compute(t, t & 1, vm_cur, masked_tag);
+        const int nx = (pp + 1) % RING;
+        stage_write(rg[nx], okb[nx], (t + 1) & 1);
+        vm_cur = vmk[nx];
         lds_barrier();
       }
     }
