@@ -53,6 +53,18 @@ va_status check_desc(const va_attn_desc* d) {
       if (strides[t][a] % vec != 0)
         return fail(VA_EINVAL, "%s stride[%d] = %lld breaks 16-byte row alignment", names[t], a,
                     (long long)strides[t][a]);
+  // The kernels address the keys of one (sequence, kv head) with 32-bit byte
+  // offsets from that region's start: positive key strides, region (plus a
+  // margin of 64 keys) under 2^31 bytes.
+  const int64_t es = d->dtype == VA_BF16 ? 2 : 4;
+  for (int t = 1; t <= 4; ++t) {
+    const int64_t keys = (t <= 2 ? (int64_t)d->L : (int64_t)d->N) + 64;
+    if (strides[t][2] <= 0)
+      return fail(VA_EUNSUPPORTED, "%s key stride must be positive (got %lld)", names[t], (long long)strides[t][2]);
+    if (keys * strides[t][2] * es > ((int64_t)1 << 31))
+      return fail(VA_EUNSUPPORTED, "%s: %lld keys x %lld-byte stride exceed the 2 GiB per-head region limit",
+                  names[t], (long long)keys - 64, (long long)(strides[t][2] * es));
+  }
   return VA_OK;
 }
 

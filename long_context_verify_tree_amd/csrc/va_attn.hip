@@ -119,6 +119,31 @@ __device__ inline int swz(int row, int chunk) {
   return chunk ^ (row & (CPR - 1));
 }
 
+// Buffer resources for K/V reads.  A raw buffer load whose byte offset is
+// at or past the resource's size returns zeros without touching memory, so
+// keys past the end of a part (and gathered indices outside [0, L), given
+// the offset kOOB) need neither clamps nor zero fills, and every load takes
+// one 32-bit offset instead of a 64-bit address.  The host keeps each K/V
+// region of one (sequence, kv head) under 2^31 bytes.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr uint32_t kOOB = 0x80000000u;
+// The base and size are wavefront-uniform; readfirstlane states it, so the
+// resource lives in scalar registers (a per-lane resource would make the
+// compiler wrap every load in a loop over distinct values).
+__device__ inline rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = (uint64_t)base;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  void* ub = (void*)(((uint64_t)hi << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(ub, (short)0, (int)__builtin_amdgcn_readfirstlane(bytes), 0x00020000);
+}
+__device__ inline u32x4 buf_load16(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+}
+__device__ inline int buf_load_i32(rsrc_t r, uint32_t off) {
+  return (int)__builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
+}
+
 #ifndef VA_RING_TILES
 #define VA_RING_TILES 2
 #endif
@@ -130,7 +155,11 @@ struct KernelShape {
   // long, so a two-tile ring fits as well.
   static constexpr bool hbm_shape = RB == 1 && ES == 2;
   static constexpr int prefetch = hbm_shape ? (D == 128 ? VA_RING_TILES : 2) : 1;
+#ifdef VA_HBM_WAVES_PER_EU
+  static constexpr int waves_per_eu = hbm_shape ? VA_HBM_WAVES_PER_EU : 1;
+#else
   static constexpr int waves_per_eu = hbm_shape && prefetch == 1 ? 2 : 1;
+#endif
 };
 
 template <class T, int D, int RB, bool GATHER>
@@ -223,29 +252,30 @@ void partial_kernel(PartialParams p) {
     }
   }
 
-  // ---- key range of this part
+  // ---- key range of this part and its buffer resources
   const T* kbase;
   const T* vbase;
-  int64_t kts, vts;
-  int kb, ke;
+  uint32_t kts_b, vts_b;     // bytes between consecutive keys
+  int ke, region;            // keys of the part; keys addressable in the region
   if (tree) {
     kbase = (const T*)p.kd + (int64_t)b * p.kds[0] + (int64_t)kvh * p.kds[1];
     vbase = (const T*)p.vd + (int64_t)b * p.vds[0] + (int64_t)kvh * p.vds[1];
-    kts = p.kds[2];
-    vts = p.vds[2];
-    kb = 0;
-    ke = p.N;
+    kts_b = (uint32_t)(p.kds[2] * ES);
+    vts_b = (uint32_t)(p.vds[2] * ES);
+    ke = region = p.N;
   } else {
     kbase = (const T*)p.kc + (int64_t)b * p.kcs[0] + (int64_t)kvh * p.kcs[1];
     vbase = (const T*)p.vc + (int64_t)b * p.vcs[0] + (int64_t)kvh * p.vcs[1];
-    kts = p.kcs[2];
-    vts = p.vcs[2];
-    kb = 0;
+    kts_b = (uint32_t)(p.kcs[2] * ES);
+    vts_b = (uint32_t)(p.vcs[2] * ES);
     ke = p.n_ctx;
+    region = p.L;
   }
+  const rsrc_t krs = make_rsrc(kbase, (uint32_t)region * kts_b);
+  const rsrc_t vrs = make_rsrc(vbase, (uint32_t)region * vts_b);
   const bool gather = GATHER && !tree;
-  const int32_t* idx_row = GATHER ? p.idx + (int64_t)b * p.idx_stride : nullptr;
-  const int ntiles = ke > kb ? (ke - kb + kTileKeys - 1) / kTileKeys : 0;
+  const rsrc_t irs = make_rsrc(GATHER ? p.idx + (int64_t)b * p.idx_stride : p.idx, GATHER ? (uint32_t)p.n_ctx * 4u : 0u);
+  const int ntiles = ke > 0 ? (ke + kTileKeys - 1) / kTileKeys : 0;
   // Context tiles are dealt out round-robin: at step k the S splits' waves
   // of this (sequence, kv head) read tiles 4(kS + part) + wave, one
   // contiguous window of 4S tiles, which keeps DRAM accesses local.  The
@@ -256,49 +286,46 @@ void partial_kernel(PartialParams p) {
   T* kt = (T*)smem + wave * WAVE_ELEMS;
   T* vt = kt + TILE_ELEMS;
 
+  // Chunk c of a lane covers key row kk0 + KPC c of the tile and the
+  // 16-byte column col of that row.
+  constexpr int KPC = 64 / CPR;
+  const int kk0 = lane / CPR;
+  const uint32_t col_b = (uint32_t)(lane % CPR) * 16u;
+
   u32x4 kreg[PF][NCH], vreg[PF][NCH];
   uint32_t vmask[PF];
+  int ixr[PF];   // gathered index of key (lane % 32) of the tile each slot loads next
 
-  // Position of context key `key` (< ke) in the cache; `ok` is false for
-  // keys past the end and for gathered indices outside [0, L).  Loads are
-  // issued for every lane (invalid ones read row 0, which always exists when
-  // a part has keys) and zeroed afterwards, so the load stream has no
-  // branches and the wait counts before each staged chunk stay partial.
-  auto key_pos = [&](int key, bool& ok) __attribute__((always_inline)) -> int64_t {
-    ok = key < ke;
-    int64_t pos = ok ? key : 0;
-    if constexpr (GATHER) {
-      if (gather) {
-        const int ix = idx_row[ok ? key : 0];
-        ok = ok && (unsigned)ix < (unsigned)p.L;
-        pos = ok ? ix : 0;
-      }
+  // Issue the loads of chunk c of tile t into one ring slot.  ix holds the
+  // gathered index of key (lane % 32) of the tile (unused when dense).
+  auto load_chunk = [&](int t, int c, int ix, u32x4& kr, u32x4& vr) __attribute__((always_inline)) {
+    const int key = kTileKeys * t + kk0 + KPC * c;
+    uint32_t ko, vo;
+    if (GATHER && gather) {
+      const int ixc = __shfl(ix, kk0 + KPC * c);
+      const bool ok = key < ke && (unsigned)ixc < (unsigned)p.L;
+      ko = ok ? (uint32_t)ixc * kts_b + col_b : kOOB;
+      vo = ok ? (uint32_t)ixc * vts_b + col_b : kOOB;
+    } else {
+      ko = (uint32_t)key * kts_b + col_b;   // past the region: reads zeros
+      vo = (uint32_t)key * vts_b + col_b;
     }
-    return pos;
+    kr = buf_load16(krs, ko);
+    vr = buf_load16(vrs, vo);
   };
-
-  // chunk c of a lane covers key row (lane + 64c) / CPR, column (lane + 64c) % CPR.
-  // The raw chunk stays in registers; whether it holds a real key is kept
-  // as bit c of `okbits` and applied when the chunk is staged, so nothing
-  // waits on the load before then.
-  auto load_chunk = [&](int t, int c, u32x4& kr, u32x4& vr, uint32_t& okbits) __attribute__((always_inline)) {
-    const int chunk = lane + 64 * c;
-    const int kk = chunk / CPR, col = chunk % CPR;
-    bool ok;
-    const int64_t pos = key_pos(kb + kTileKeys * t + kk, ok);
-    kr = *(const u32x4*)(kbase + pos * kts + col * VEC);
-    vr = *(const u32x4*)(vbase + pos * vts + col * VEC);
-    okbits = (okbits & ~(1u << c)) | ((uint32_t)ok << c);
-  };
-  auto tile_mask = [&](int t) __attribute__((always_inline)) -> uint32_t {
-    bool mine;
-    key_pos(kb + kTileKeys * t + n, mine);
-    return (uint32_t)__ballot(mine && h == 0);
-  };
-  auto load_tile = [&](int t, u32x4 (&kr)[NCH], u32x4 (&vr)[NCH], uint32_t& vm, uint32_t& okbits) __attribute__((always_inline)) {
+  auto load_tile = [&](int t, int ix, u32x4 (&kr)[NCH], u32x4 (&vr)[NCH]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int c = 0; c < NCH; ++c) load_chunk(t, c, kr[c], vr[c], okbits);
-    vm = tile_mask(t);
+    for (int c = 0; c < NCH; ++c) load_chunk(t, c, ix, kr[c], vr[c]);
+  };
+  // Keys of tile t that exist (bit j: key 32t + j), from lane n's index.
+  auto tile_mask = [&](int t, int ix) __attribute__((always_inline)) -> uint32_t {
+    bool ok = kTileKeys * t + n < ke;
+    if (GATHER && gather) ok = ok && (unsigned)ix < (unsigned)p.L;
+    return (uint32_t)__ballot(ok && h == 0);
+  };
+  auto load_idx = [&](int t) __attribute__((always_inline)) -> int {
+    if constexpr (GATHER) return buf_load_i32(irs, (uint32_t)(kTileKeys * t + n) * 4u);
+    return 0;
   };
 
   // ---- online softmax state
@@ -460,51 +487,59 @@ void partial_kernel(PartialParams p) {
   // after it.
   const int nw = tfirst < ntiles ? (ntiles - 1 - tfirst) / tstep + 1 : 0;   // tiles of this wavefront
   const int klast = nw > 0 ? nw - 1 : 0;
-  uint32_t okbits[PF];
+  auto tile_of = [&](int k) __attribute__((always_inline)) -> int { return tfirst + (k < klast ? k : klast) * tstep; };
 #pragma unroll
   for (int pp = 0; pp < PF; ++pp) {
-    okbits[pp] = 0;
-    load_tile(tfirst + (pp < klast ? pp : klast) * tstep, kreg[pp], vreg[pp], vmask[pp], okbits[pp]);
+    const int ix = load_idx(tile_of(pp));
+    load_tile(tile_of(pp), ix, kreg[pp], vreg[pp]);
+    vmask[pp] = tile_mask(tile_of(pp), ix);
+    ixr[pp] = load_idx(tile_of(pp + PF));
   }
+  // Stage ring slot pp in the wavefront's LDS tile; with reload, re-issue
+  // each chunk for tile tn right after it is staged.
   auto stage = [&](int pp, bool reload, int tn) __attribute__((always_inline)) {
 #pragma unroll
     for (int cc = 0; cc < NCH; ++cc) {
-      const int chunk = lane + 64 * cc;
-      const int kk = chunk / CPR, col = chunk % CPR;
+      const int kk = kk0 + KPC * cc, col = lane % CPR;
       const int off = kk * D + swz<CPR>(kk, col) * VEC;
-      const bool ok = (okbits[pp] >> cc) & 1u;
-      const u32x4 z = u32x4{0, 0, 0, 0};
-      *(u32x4*)(kt + off) = ok ? kreg[pp][cc] : z;
-      *(u32x4*)(vt + off) = ok ? vreg[pp][cc] : z;
-      if (reload) load_chunk(tn, cc, kreg[pp][cc], vreg[pp][cc], okbits[pp]);
+      *(u32x4*)(kt + off) = kreg[pp][cc];
+      *(u32x4*)(vt + off) = vreg[pp][cc];
+      if (reload) load_chunk(tn, cc, ixr[pp], kreg[pp][cc], vreg[pp][cc]);
     }
   };
-  auto run_tile = [&](int tp, uint32_t vm) __attribute__((always_inline)) {
-    if constexpr (KernelShape<RB, ES, D>::hbm_shape) {
-      if (!tree && vm == ~0u)
-        compute(tp, vm, std::false_type{});
-      else
-        compute(tp, vm, std::true_type{});
-    } else {
-      compute(tp, vm, std::true_type{});
-    }
-  };
-  int k = 0;
-  for (; k + PF <= nw; k += PF) {
+  // Whole ring turns over this wavefront's tiles [0, k_end) with one compute
+  // variant; returns the first tile not taken.  The loop body has no early
+  // exit and no second compute variant: either would make the compiler
+  // drain the ring or duplicate the accumulators across the branches.
+  auto ring_loop = [&](int k_end, auto masked_tag) __attribute__((always_inline)) -> int {
+    int k = 0;
+    for (; k + PF <= k_end; k += PF) {
 #pragma unroll
-    for (int pp = 0; pp < PF; ++pp) {
-      const uint32_t vm = vmask[pp];
-      const int kn = k + pp + PF < klast ? k + pp + PF : klast;
-      stage(pp, true, tfirst + kn * tstep);
-      vmask[pp] = tile_mask(tfirst + kn * tstep);
-      run_tile(tfirst + (k + pp) * tstep, vm);
+      for (int pp = 0; pp < PF; ++pp) {
+        const uint32_t vm = vmask[pp];
+        const int tn = tile_of(k + pp + PF);
+        stage(pp, true, tn);
+        vmask[pp] = tile_mask(tn, ixr[pp]);
+        ixr[pp] = load_idx(tile_of(k + pp + 2 * PF));
+        compute(tfirst + (k + pp) * tstep, vm, masked_tag);
+      }
     }
+    return k;
+  };
+  int k;
+  if (!tree && !gather) {
+    // dense context: every tile but the part's last is whole (no mask)
+    const bool partial_last = (ke % kTileKeys) != 0 && nw > 0 && tfirst + (nw - 1) * tstep == ntiles - 1;
+    k = ring_loop(nw - (partial_last ? 1 : 0), std::false_type{});
+  } else {
+    k = ring_loop(nw, std::true_type{});
   }
+  // the last (at most PF) tiles, already in their ring slots
 #pragma unroll
-  for (int pp = 0; pp < PF - 1; ++pp) {
+  for (int pp = 0; pp < PF; ++pp) {
     if (k + pp < nw) {
       stage(pp, false, 0);
-      run_tile(tfirst + (k + pp) * tstep, vmask[pp]);
+      compute(tfirst + (k + pp) * tstep, vmask[pp], std::true_type{});
     }
   }
 
@@ -650,75 +685,72 @@ void rows_kernel(PartialParams p) {
 
   const T* kbase;
   const T* vbase;
-  int64_t kts, vts;
-  int kb, ke;
+  uint32_t kts_b, vts_b;     // bytes between consecutive keys
+  int kb, ke, region;        // key range of the part; keys addressable in the region
   if (tree) {
     kbase = (const T*)p.kd + (int64_t)b * p.kds[0] + (int64_t)kvh * p.kds[1];
     vbase = (const T*)p.vd + (int64_t)b * p.vds[0] + (int64_t)kvh * p.vds[1];
-    kts = p.kds[2];
-    vts = p.vds[2];
+    kts_b = (uint32_t)(p.kds[2] * 2);
+    vts_b = (uint32_t)(p.vds[2] * 2);
     kb = 0;
-    ke = p.N;
+    ke = region = p.N;
   } else {
     kbase = (const T*)p.kc + (int64_t)b * p.kcs[0] + (int64_t)kvh * p.kcs[1];
     vbase = (const T*)p.vc + (int64_t)b * p.vcs[0] + (int64_t)kvh * p.vcs[1];
-    kts = p.kcs[2];
-    vts = p.vcs[2];
+    kts_b = (uint32_t)(p.kcs[2] * 2);
+    vts_b = (uint32_t)(p.vcs[2] * 2);
     kb = part * p.split_len;
     ke = min(p.n_ctx, kb + p.split_len);
+    region = p.L;
   }
+  const rsrc_t krs = make_rsrc(kbase, (uint32_t)region * kts_b);
+  const rsrc_t vrs = make_rsrc(vbase, (uint32_t)region * vts_b);
   const bool gather = GATHER && !tree;
-  const int32_t* idx_row = GATHER ? p.idx + (int64_t)b * p.idx_stride : nullptr;
+  const rsrc_t irs = make_rsrc(GATHER ? p.idx + (int64_t)b * p.idx_stride : p.idx, GATHER ? (uint32_t)p.n_ctx * 4u : 0u);
   const int ntiles = ke > kb ? (ke - kb + kTileKeys - 1) / kTileKeys : 0;
 
-  auto key_pos = [&](int key, bool& ok) __attribute__((always_inline)) -> int64_t {
-    ok = key < ke;
-    int64_t pos = ok ? key : kb;
-    if constexpr (GATHER) {
-      if (gather) {
-        const int ix = idx_row[ok ? key : kb];
-        ok = ok && (unsigned)ix < (unsigned)p.L;
-        pos = ok ? ix : 0;
-      }
-    }
-    return pos;
-  };
-
   // Thread chunk j of a tile: combined index tid + 512 j; the first KCH are
-  // K chunks, the rest V chunks; chunk -> (key row, 16-byte column).
+  // K chunks, the rest V chunks.  Every chunk of a thread lies in the same
+  // key row kk_t of the tile, at 16-byte column col_t.  Whether a chunk is a
+  // K or a V chunk depends only on the wavefront.
+  const int kk_t = (tid % KCH) / CPR;
+  const int col_t = (tid % KCH) % CPR;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   u32x4 rg[RING][NCT];
-  uint32_t okb[RING], vmk[RING];
-  auto load = [&](int t, u32x4 (&rx)[NCT], uint32_t& ok_bits, uint32_t& vm) __attribute__((always_inline)) {
-    const int tc = t < ntiles ? t : (ntiles > 0 ? ntiles - 1 : 0);   // past the end: refetch, never staged
-    ok_bits = 0;
+  bool okr[RING];   // the thread's key exists (tile slot)
+  int ixr[RING];    // gathered index of the thread's key in the tile the slot loads next
+  auto clamp_tile = [&](int t) __attribute__((always_inline)) -> int {
+    return t < ntiles ? t : (ntiles > 0 ? ntiles - 1 : 0);   // past the end: refetch, never staged
+  };
+  auto load_idx = [&](int t) __attribute__((always_inline)) -> int {
+    if constexpr (GATHER) return buf_load_i32(irs, (uint32_t)(kb + kTileKeys * clamp_tile(t) + kk_t) * 4u);
+    return 0;
+  };
+  auto load = [&](int t, int ix, u32x4 (&rx)[NCT], bool& ok) __attribute__((always_inline)) {
+    const int key = kb + kTileKeys * clamp_tile(t) + kk_t;
+    ok = key < ke;
+    uint32_t ko = (uint32_t)key * kts_b, vo = (uint32_t)key * vts_b;
+    if (GATHER && gather) {
+      ok = ok && (unsigned)ix < (unsigned)p.L;
+      ko = ok ? (uint32_t)ix * kts_b : kOOB;
+      vo = ok ? (uint32_t)ix * vts_b : kOOB;
+    }
 #pragma unroll
     for (int j = 0; j < NCT; ++j) {
-      const int ci = tid + kRowsThreads * j;
-      const bool isv = ci >= KCH;
-      const int ch = isv ? ci - KCH : ci;
-      const int kk = ch / CPR, col = ch % CPR;
-      bool ok;
-      const int64_t pos = key_pos(kb + kTileKeys * tc + kk, ok);
-      const T* src = isv ? vbase + pos * vts : kbase + pos * kts;
-      rx[j] = *(const u32x4*)(src + col * VEC);
-      ok_bits |= (uint32_t)ok << j;
+      const bool isv = 64 * wave_u + kRowsThreads * j >= KCH;
+      rx[j] = buf_load16(isv ? vrs : krs, (isv ? vo : ko) + (uint32_t)col_t * 16u);
     }
-    bool mine;
-    key_pos(kb + kTileKeys * tc + n, mine);
-    vm = (uint32_t)__ballot(mine && h == 0);
   };
-  auto stage_write = [&](const u32x4 (&rx)[NCT], uint32_t ok_bits, int buf) __attribute__((always_inline)) {
+  __shared__ int kval[2][kTileKeys];   // key of the staged tile exists
+  auto stage_write = [&](const u32x4 (&rx)[NCT], bool ok, int buf) __attribute__((always_inline)) {
     T* base = stage + buf * STAGE_ELEMS;
 #pragma unroll
     for (int j = 0; j < NCT; ++j) {
-      const int ci = tid + kRowsThreads * j;
-      const bool isv = ci >= KCH;
-      const int ch = isv ? ci - KCH : ci;
-      const int kk = ch / CPR, col = ch % CPR;
-      const int off = (isv ? TILE_ELEMS : 0) + kk * D + swz<CPR>(kk, col) * VEC;
-      const bool ok = (ok_bits >> j) & 1u;
-      *(u32x4*)(base + off) = ok ? rx[j] : u32x4{0, 0, 0, 0};
+      const bool isv = 64 * wave_u + kRowsThreads * j >= KCH;
+      const int off = (isv ? TILE_ELEMS : 0) + kk_t * D + swz<CPR>(kk_t, col_t) * VEC;
+      *(u32x4*)(base + off) = rx[j];
     }
+    if (tid < KCH && col_t == 0) kval[buf][kk_t] = ok;
   };
 
   float m_run = -INFINITY, l_run = 0.f;
@@ -729,11 +761,13 @@ void rows_kernel(PartialParams p) {
     for (int e = 0; e < 16; ++e) o[db][e] = 0.f;
   const float c = p.c;
 
-  auto compute = [&](int t, int buf, uint32_t vm, auto masked_tag) __attribute__((always_inline)) {
+  auto compute = [&](int t, int buf, auto masked_tag) __attribute__((always_inline)) {
     constexpr bool MASKED = decltype(masked_tag)::value;
     const T* kt = stage + buf * STAGE_ELEMS;
     const T* vt = kt + TILE_ELEMS;
-    const uint32_t key_bits = MASKED ? vm & anc[32 * wave + n][t & (kAncWords - 1)] : ~0u;
+    uint32_t key_bits = ~0u;
+    if constexpr (MASKED)
+      key_bits = (uint32_t)__ballot(kval[buf][n] != 0 && h == 0) & anc[32 * wave + n][t & (kAncWords - 1)];
 
     f32x16 s;
 #pragma unroll
@@ -803,10 +837,13 @@ void rows_kernel(PartialParams p) {
 
   // prologue: tiles 0..RING-1 in flight, tile 0 staged
 #pragma unroll
-  for (int pp = 0; pp < RING; ++pp) load(pp, rg[pp], okb[pp], vmk[pp]);
-  stage_write(rg[0], okb[0], 0);
-  uint32_t vm_cur = vmk[0];
-  load(RING, rg[0], okb[0], vmk[0]);
+  for (int pp = 0; pp < RING; ++pp) {
+    load(pp, load_idx(pp), rg[pp], okr[pp]);
+    ixr[pp] = load_idx(pp + RING);
+  }
+  stage_write(rg[0], okr[0], 0);
+  load(RING, ixr[0], rg[0], okr[0]);
+  ixr[0] = load_idx(2 * RING);
   lds_barrier();
 
   // Tiles [0, t_end): compute tile t from LDS buffer t & 1, then stage tile
@@ -821,11 +858,11 @@ void rows_kernel(PartialParams p) {
 #pragma unroll
       for (int pp = 0; pp < RING; ++pp) {
         const int t = t0 + pp;
-        compute(t, t & 1, vm_cur, masked_tag);
+        compute(t, t & 1, masked_tag);
         const int nx = (pp + 1) % RING;
-        stage_write(rg[nx], okb[nx], (t + 1) & 1);
-        vm_cur = vmk[nx];
-        load(t + 1 + RING, rg[nx], okb[nx], vmk[nx]);
+        stage_write(rg[nx], okr[nx], (t + 1) & 1);
+        load(t + 1 + RING, ixr[nx], rg[nx], okr[nx]);
+        ixr[nx] = load_idx(t + 1 + 2 * RING);
         lds_barrier();
       }
     }
@@ -833,10 +870,9 @@ void rows_kernel(PartialParams p) {
     for (int pp = 0; pp < RING - 1; ++pp) {
       const int t = t0 + pp;
       if (t < t_end) {
-        compute(t, t & 1, vm_cur, masked_tag);
+        compute(t, t & 1, masked_tag);
         const int nx = (pp + 1) % RING;
-        stage_write(rg[nx], okb[nx], (t + 1) & 1);
-        vm_cur = vmk[nx];
+        stage_write(rg[nx], okr[nx], (t + 1) & 1);
         lds_barrier();
       }
     }
@@ -847,8 +883,12 @@ void rows_kernel(PartialParams p) {
     // whole tiles without the mask, then the partial tail tile (already
     // staged in buffer nfull & 1 by the loop) with it
     const int nfull = (ke - kb) / kTileKeys;
-    tile_loop(nfull, std::false_type{});
-    if (nfull < ntiles) compute(nfull, nfull & 1, vm_cur, std::true_type{});
+    if (gather) {
+      tile_loop(ntiles, std::true_type{});
+    } else {
+      tile_loop(nfull, std::false_type{});
+      if (nfull < ntiles) compute(nfull, nfull & 1, std::true_type{});
+    }
   }
 
   // this wavefront's rows: normalised partial and log2-sum-exp
