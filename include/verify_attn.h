@@ -86,7 +86,11 @@ typedef enum va_dtype {
  * Each tensor is addressed with element strides over its three outer axes
  * (batch, head, row); the innermost (D) stride is 1.  Token-major caches
  * ([B, L, Hkv, D]) are expressed through the strides.  Base pointers and all
- * strides must keep every row 16-byte aligned. */
+ * strides must keep every row 16-byte aligned.  The key (token / node)
+ * strides of the four K/V tensors must be positive, and the keys of one
+ * (sequence, kv head) plus 64 must span under 2 GiB: (L + 64) x key stride
+ * bytes for the cache, (N + 64) x key stride bytes for the draft tensors
+ * (else VA_EUNSUPPORTED); the kernels address them with 32-bit offsets. */
 typedef struct va_attn_desc {
   int32_t B;            /* sequences, >= 1                                     */
   int32_t Hq;           /* query heads, >= 1, multiple of Hkv                  */

@@ -91,6 +91,19 @@ def test_workspace_size_and_validation(ops):
     bad = good_desc(ops)
     bad.kc_stride = (ctypes.c_int64 * 3)(2 * 1000 * 128, 1000 * 128, 100)   # rows not 16-byte aligned
     assert ws_size(ops, bad, 0)[0] == ops.VA_EINVAL
+    # keys are addressed with 32-bit byte offsets inside one (sequence, kv head) region
+    for attr in ("kc_stride", "vc_stride", "kd_stride", "vd_stride"):
+        for key_stride in (0, -128):
+            bad = good_desc(ops)
+            setattr(bad, attr, (ctypes.c_int64 * 3)(0, 0, key_stride))
+            assert ws_size(ops, bad, 0)[0] == ops.VA_EUNSUPPORTED, (attr, key_stride)
+    big = good_desc(ops, L=(1 << 23) - 64)         # (L + 64) * 256 B = 2 GiB: the largest accepted region
+    assert ws_size(ops, big, 0)[0] == ops.VA_OK
+    big = good_desc(ops, L=(1 << 23) - 63)
+    assert ws_size(ops, big, 0)[0] == ops.VA_EUNSUPPORTED
+    wide = good_desc(ops, L=1 << 20)               # token-major cache: 8 heads x 128 per key -> 2 KiB stride
+    wide.kc_stride = (ctypes.c_int64 * 3)(1 << 30, 128, 1024)
+    assert ws_size(ops, wide, 0)[0] == ops.VA_EUNSUPPORTED
 
 
 FAKE = ctypes.c_void_p(0x100000)   # never dereferenced: every call below fails validation first
