@@ -3,17 +3,26 @@
 // window, take the top-m tokens by draft-lookahead score, then fill the rest
 // of the budget with the best remaining tokens by target-historical score.
 //
-// One workgroup of 1024 threads per sequence.  Each tier is an exact top-r
-// over the contiguous candidate range [lo, hi) between sink and window:
+// One workgroup of 1024 threads per sequence.  The row is cut into segments
+// of 32768 tokens; in each segment thread t owns the 32 consecutive tokens
+// 32t .. 32t+31, so "lower index first" is thread order and then bit order,
+// and one 32-bit word per thread and segment holds the thread's selection
+// marks.  Each tier is an exact top-r over the candidates (tokens between
+// sink and window, minus those already taken):
 //   * scores become order-preserving 32-bit keys (NaN lowest, -0 == +0);
-//   * four 8-bit radix passes (LDS histograms, integer atomics, so the counts
-//     do not depend on thread order) find the key T of the r-th best token
-//     and the number of tokens strictly above it;
-//   * one ordered pass marks every token above T and the first tokens equal
-//     to T in index order (a block-wide prefix count), which is the
-//     lower-index tie rule.
-// The marks live in a bitmap in LDS; a final ordered compaction writes the
-// union of sink, window and both tiers as an ascending index list.
+//   * three radix passes (12, 10 and 10 bits) over LDS histograms (integer
+//     atomics, so counts do not depend on thread order) find the key T of the
+//     r-th best candidate and the number of candidates strictly above it.
+//     The first pass of both tiers shares one sweep: the target histogram
+//     counts every free token, and the draft tier's picks are subtracted
+//     from it before the target tier starts;
+//   * one block-wide exclusive scan of each thread's count of keys equal to
+//     T gives every such token its rank in index order; the first ones up to
+//     r are taken (the lower-index tie rule).
+// A last block scan of the per-thread mark counts (plus sink and window)
+// writes the ascending index list.  A row of one segment keeps its keys in
+// registers for all passes; longer rows re-read each segment per pass (the
+// row then sits in L2).
 
 #include <stdint.h>
 
@@ -24,8 +33,10 @@
 namespace va {
 namespace {
 
-constexpr int kST = 1024;
+constexpr int kST = 1024;                 // threads per workgroup
 constexpr int kSWaves = kST / 64;
+constexpr int kKPT = 32;                  // tokens per thread per segment
+constexpr int kSeg = kST * kKPT;          // tokens per segment
 
 struct SelParams {
   const float* ds;
@@ -42,14 +53,17 @@ __device__ inline uint32_t order_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Exclusive prefix count of `pred` over the workgroup in thread order; sets
-// *total.  Uses wsum[kSWaves]; contains two barriers.
-__device__ inline int block_prefix_count(bool pred, int* wsum, int* total) {
+// Exclusive prefix sum of v over the workgroup in thread order; *total gets
+// the sum.  Uses wsum[kSWaves]; two barriers.
+__device__ inline int block_excl_scan(int v, int* wsum, int* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const uint64_t bal = __ballot(pred);
-  const uint64_t below = lane ? (bal & (~0ull >> (64 - lane))) : 0ull;
-  const int in_wave = __popcll(below);
-  if (lane == 0) wsum[wave] = __popcll(bal);
+  int x = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(x, off);
+    if (lane >= off) x += y;
+  }
+  if (lane == 63) wsum[wave] = x;
   __syncthreads();
   int before = 0, tot = 0;
 #pragma unroll
@@ -60,79 +74,65 @@ __device__ inline int block_prefix_count(bool pred, int* wsum, int* total) {
   }
   __syncthreads();
   *total = tot;
-  return before + in_wave;
+  return before + x - v;
 }
 
-__device__ inline bool marked(const uint32_t* bm, int j) { return (bm[j >> 5] >> (j & 31)) & 1u; }
+// Radix digits of a 32-bit key: 12 bits, then 10, then 10.
+constexpr int kDigitBits[3] = {12, 10, 10};
+constexpr int kDigitShift[3] = {20, 10, 0};
+constexpr int kBins0 = 1 << 12;
 
-// Marks the top `r` tokens of [lo, hi) by `score` (skipping already marked
-// tokens when `skip_marked`).
-__device__ void select_tier(const float* score, int lo, int hi, int r, bool skip_marked, uint32_t* bm,
-                            int* hist, int* wsum, int* shared2) {
-  if (r <= 0) return;
+struct SelShared {
+  int hist_d[kBins0];        // first-digit histogram of the draft tier
+  int hist_t[kBins0];        // first-digit histogram of the target tier; later digits reuse hist_d
+  int wsum[kSWaves];
+  int pick[2];               // digit, candidates in higher buckets
+};
+
+// Bits of the 32 tokens [j0, j0 + 32) that lie in [lo, hi).
+__device__ inline uint32_t range_bits(int j0, int lo, int hi) {
+  const int a = lo - j0, e = hi - j0;   // bit i set for a <= i < e
+  const uint32_t below_e = e <= 0 ? 0u : (e >= 32 ? ~0u : (1u << e) - 1u);
+  const uint32_t below_a = a <= 0 ? 0u : (a >= 32 ? ~0u : (1u << a) - 1u);
+  return below_e & ~below_a;
+}
+
+// Given a histogram of `nbins` buckets (nbins / kST per thread, highest
+// buckets at the lowest threads) and `above` candidates in higher buckets
+// already, finds the bucket holding the r-th largest candidate: sets
+// sh.pick = {bucket, candidates above it}.  Three barriers; every thread
+// reads the result after the last.
+__device__ inline void pick_bucket(const int* hist, int nbins, int r, int above, SelShared& sh) {
   const int tid = threadIdx.x;
-  uint32_t prefix = 0;
-  int above = 0;
-  for (int pass = 0; pass < 4; ++pass) {
-    const int shift = 24 - 8 * pass;
-    for (int d = tid; d < 256; d += kST) hist[d] = 0;
-    __syncthreads();
-    for (int j = lo + tid; j < hi; j += kST) {
-      if (skip_marked && marked(bm, j)) continue;
-      const uint32_t u = order_key(score[j]);
-      if (pass > 0 && (u >> (shift + 8)) != (prefix >> (shift + 8))) continue;
-      atomicAdd(&hist[(u >> shift) & 255u], 1);
-    }
-    __syncthreads();
-    if (tid == 0) {
-      int cum = above, digit = 0;
-      for (int d = 255; d >= 0; --d) {
-        if (cum + hist[d] >= r) {
-          digit = d;
-          break;
-        }
-        cum += hist[d];
-      }
-      shared2[0] = digit;
-      shared2[1] = cum;
-    }
-    __syncthreads();
-    prefix |= (uint32_t)shared2[0] << shift;
-    above = shared2[1];
-    __syncthreads();
+  const int per = nbins / kST;   // 4 or 1
+  const int top = nbins - per * tid;   // this thread's buckets: [top - per, top)
+  int c[4] = {0, 0, 0, 0};
+  int csum = 0;
+  for (int k = 0; k < per; ++k) {
+    c[k] = hist[top - 1 - k];
+    csum += c[k];
   }
-  const uint32_t T = prefix;
-  const int need_eq = r - above;  // >= 1 tokens equal to T, lowest indices first
-  int taken_eq = 0;
-  for (int base = lo; base < hi; base += kST) {
-    const int j = base + tid;
-    bool valid = j < hi;
-    if (valid && skip_marked && marked(bm, j)) valid = false;
-    const uint32_t u = valid ? order_key(score[j]) : 0u;
-    const bool gt = valid && u > T;
-    const bool eq = valid && u == T;
-    int tot;
-    const int before = block_prefix_count(eq, wsum, &tot);
-    const bool take = gt || (eq && taken_eq + before < need_eq);
-    if (take) atomicOr(&bm[j >> 5], 1u << (j & 31));
-    taken_eq += tot;
-    if (taken_eq >= need_eq && base + kST < hi) {
-      // Remaining equal keys are not taken; only larger keys still are.
-      for (int j2 = base + kST + tid; j2 < hi; j2 += kST) {
-        if (skip_marked && marked(bm, j2)) continue;
-        if (order_key(score[j2]) > T) atomicOr(&bm[j2 >> 5], 1u << (j2 & 31));
+  int tot;
+  int cum = above + block_excl_scan(csum, sh.wsum, &tot);
+  if (cum < r && cum + csum >= r) {
+    int bucket = top - 1;
+    for (int k = 0; k < per; ++k) {
+      if (cum + c[k] >= r) {
+        bucket = top - 1 - k;
+        break;
       }
-      break;
+      cum += c[k];
     }
+    sh.pick[0] = bucket;
+    sh.pick[1] = cum;
   }
   __syncthreads();
 }
 
+template <bool RESIDENT>
 __global__ __launch_bounds__(kST) void select_kernel(SelParams p) {
-  extern __shared__ uint32_t bm[];
-  __shared__ int hist[256];
-  __shared__ int wsum[kSWaves];
-  __shared__ int shared2[2];
+  extern __shared__ uint32_t marks[];   // [nseg][kST]: tokens taken by the two tiers
+  __shared__ SelShared sh;
   const int tid = threadIdx.x;
   const int b = blockIdx.x;
   const float* ds = p.ds + (int64_t)b * p.ld;
@@ -152,20 +152,143 @@ __global__ __launch_bounds__(kST) void select_kernel(SelParams p) {
   int r1 = p.top_m < rest ? p.top_m : rest;
   r1 = r1 < n_free ? r1 : n_free;
   const int r2 = rest - r1;
+  const int nseg = RESIDENT ? 1 : (L + kSeg - 1) / kSeg;
 
-  const int words = (L + 31) >> 5;
-  for (int i = tid; i < words; i += kST) bm[i] = 0u;
+  for (int s = 0; s < nseg; ++s) marks[s * kST + tid] = 0u;
+  for (int i = tid; i < kBins0; i += kST) {
+    sh.hist_d[i] = 0;
+    sh.hist_t[i] = 0;
+  }
+
+  uint32_t kd[kKPT], kt[kKPT];
+  auto load_keys = [&](const float* row, int s, uint32_t (&key)[kKPT]) __attribute__((always_inline)) {
+    const int j0 = s * kSeg + tid * kKPT;
+    const bool vec = j0 + kKPT <= L && ((reinterpret_cast<uintptr_t>(row + j0) & 15u) == 0);
+    if (vec) {
+#pragma unroll
+      for (int q = 0; q < kKPT / 4; ++q) {
+        const float4 v = *reinterpret_cast<const float4*>(row + j0 + 4 * q);
+        key[4 * q + 0] = order_key(v.x);
+        key[4 * q + 1] = order_key(v.y);
+        key[4 * q + 2] = order_key(v.z);
+        key[4 * q + 3] = order_key(v.w);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < kKPT; ++i) key[i] = j0 + i < L ? order_key(row[j0 + i]) : 0u;
+    }
+  };
+  auto free_bits = [&](int s) __attribute__((always_inline)) -> uint32_t {
+    return range_bits(s * kSeg + tid * kKPT, lo, hi);
+  };
+
+  // first digit of both tiers in one sweep; the target histogram counts
+  // every free token and is corrected for the draft tier's picks later
+  if (RESIDENT) {
+    load_keys(ds, 0, kd);
+    load_keys(ts, 0, kt);
+  }
   __syncthreads();
-  select_tier(ds, lo, hi, r1, false, bm, hist, wsum, shared2);
-  select_tier(ts, lo, hi, r2, true, bm, hist, wsum, shared2);
+  for (int s = 0; s < nseg; ++s) {
+    if (!RESIDENT) {
+      load_keys(ds, s, kd);
+      load_keys(ts, s, kt);
+    }
+    const uint32_t cand = free_bits(s);
+#pragma unroll
+    for (int i = 0; i < kKPT; ++i) {
+      if ((cand >> i) & 1u) {
+        if (r1 > 0) atomicAdd(&sh.hist_d[kd[i] >> kDigitShift[0]], 1);
+        if (r2 > 0) atomicAdd(&sh.hist_t[kt[i] >> kDigitShift[0]], 1);
+      }
+    }
+  }
+  __syncthreads();
 
+  // Marks the top r candidates (free tokens not yet marked) of a tier whose
+  // first-digit histogram is hist0; key holds the keys when resident.
+  auto tier = [&](const float* row, int r, int* hist0, uint32_t (&key)[kKPT]) __attribute__((always_inline)) {
+    uint32_t prefix = 0;
+    int above = 0;
+    pick_bucket(hist0, kBins0, r, 0, sh);
+    prefix = (uint32_t)sh.pick[0] << kDigitShift[0];
+    above = sh.pick[1];
+    for (int pass = 1; pass < 3; ++pass) {
+      const int shift = kDigitShift[pass];
+      const int nb = 1 << kDigitBits[pass];
+      const int hs = shift + kDigitBits[pass];   // bits above this digit are fixed
+      __syncthreads();   // everyone has read pick before the histogram is reused
+      for (int i = tid; i < nb; i += kST) sh.hist_d[i] = 0;
+      __syncthreads();
+      for (int s = 0; s < nseg; ++s) {
+        if (!RESIDENT) load_keys(row, s, key);
+        const uint32_t cand = free_bits(s) & ~marks[s * kST + tid];
+#pragma unroll
+        for (int i = 0; i < kKPT; ++i) {
+          if (((cand >> i) & 1u) && (key[i] >> hs) == (prefix >> hs))
+            atomicAdd(&sh.hist_d[(key[i] >> shift) & (uint32_t)(nb - 1)], 1);
+        }
+      }
+      __syncthreads();
+      pick_bucket(sh.hist_d, nb, r, above, sh);
+      prefix |= (uint32_t)sh.pick[0] << shift;
+      above = sh.pick[1];
+    }
+    // every candidate above T, and the first (r - above) equal to T in
+    // index order
+    const uint32_t T = prefix;
+    const int need_eq = r - above;
+    int seen_eq = 0;
+    for (int s = 0; s < nseg; ++s) {
+      if (!RESIDENT) load_keys(row, s, key);
+      const uint32_t cand = free_bits(s) & ~marks[s * kST + tid];
+      uint32_t gt = 0, eq = 0;
+#pragma unroll
+      for (int i = 0; i < kKPT; ++i) {
+        const bool c = (cand >> i) & 1u;
+        gt |= (uint32_t)(c && key[i] > T) << i;
+        eq |= (uint32_t)(c && key[i] == T) << i;
+      }
+      int tot;
+      const int before = seen_eq + block_excl_scan(__popc(eq), sh.wsum, &tot);
+      int take = need_eq - before;   // equal keys this thread may still take
+      uint32_t eq_taken = 0;
+      for (uint32_t e = eq; e && take > 0; e &= e - 1, --take) eq_taken |= e & (~e + 1u);
+      marks[s * kST + tid] |= gt | eq_taken;
+      seen_eq += tot;
+    }
+  };
+
+  if (r1 > 0) tier(ds, r1, sh.hist_d, kd);
+  if (r2 > 0) {
+    if (r1 > 0) {
+      // take the draft tier's picks out of the target histogram
+      for (int s = 0; s < nseg; ++s) {
+        if (!RESIDENT) load_keys(ts, s, kt);
+        const uint32_t m = marks[s * kST + tid];
+#pragma unroll
+        for (int i = 0; i < kKPT; ++i)
+          if ((m >> i) & 1u) atomicSub(&sh.hist_t[kt[i] >> kDigitShift[0]], 1);
+      }
+      __syncthreads();
+    }
+    tier(ts, r2, sh.hist_t, kt);
+  }
+
+  // ascending output: sink, both tiers and window
   int written = 0;
-  for (int base = 0; base < L; base += kST) {
-    const int j = base + tid;
-    const bool sel = j < L && (j < lo || j >= hi || marked(bm, j));
+  for (int s = 0; s < nseg; ++s) {
+    const int j0 = s * kSeg + tid * kKPT;
+    const uint32_t valid = range_bits(j0, 0, L);
+    const uint32_t sel = (marks[s * kST + tid] | (valid & ~range_bits(j0, lo, hi))) & valid;
     int tot;
-    const int before = block_prefix_count(sel, wsum, &tot);
-    if (sel && written + before < p.k_out) out[written + before] = j;
+    const int before = written + block_excl_scan(__popc(sel), sh.wsum, &tot);
+    int pos = before;
+    for (uint32_t e = sel; e; e &= e - 1) {
+      const int i = __ffs(e) - 1;
+      if (pos < p.k_out) out[pos] = j0 + i;
+      ++pos;
+    }
     written += tot;
   }
 }
@@ -188,13 +311,18 @@ hipError_t launch_select(const float* draft_score, const float* target_score, in
   p.top_m = top_m;
   p.budget = budget;
   p.k_out = budget < L ? budget : L;
-  const size_t lds = budget < L ? (size_t)((L + 31) / 32) * 4 : 4;
+  const int nseg = (L + kSeg - 1) / kSeg;
+  const size_t lds = (size_t)(nseg > 0 ? nseg : 1) * kST * sizeof(uint32_t);
+  const bool resident = nseg <= 1;
+  const void* fn = resident ? (const void*)select_kernel<true> : (const void*)select_kernel<false>;
   if (lds > 48 * 1024) {
-    hipError_t e = hipFuncSetAttribute((const void*)select_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)lds);
+    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(select_kernel, dim3(B), dim3(kST), lds, stream, p);
+  if (resident)
+    hipLaunchKernelGGL(select_kernel<true>, dim3(B), dim3(kST), lds, stream, p);
+  else
+    hipLaunchKernelGGL(select_kernel<false>, dim3(B), dim3(kST), lds, stream, p);
   return hipGetLastError();
 }
 

@@ -241,6 +241,24 @@ def test_selector_ties_specials_and_special_cases(gpu_lib):
                               (4, 16, 10, 20), (7, 3, 9999, 4000), (4, 16, 10, L), (4, 16, 10, L + 9)):
         got = _sel_gpu(gpu_lib, d, t, S, W, m, budget)
         np.testing.assert_array_equal(got, vo.select_verify_set(d, t, S, W, m, budget), err_msg=str((S, W, m, budget)))
+    say("case selector multi-segment ties, unaligned rows")
+    # rows longer than one 32768-token segment (re-read per pass), a ragged
+    # last segment, ties across segment borders, and a row stride that leaves
+    # rows unaligned to 16 bytes
+    L2, ld = 70001, 70003
+    d = levels[rng.integers(2, len(levels), (2, L2))]
+    t = rng.lognormal(0, 2, (2, L2)).astype(np.float32)
+    t[:, 30000:40000] = 3.0
+    dpad = torch.zeros(2, ld, dtype=torch.float32)
+    tpad = torch.zeros(2, ld, dtype=torch.float32)
+    dpad[:, :L2] = torch.from_numpy(d)
+    tpad[:, :L2] = torch.from_numpy(t)
+    dv, tv = dpad.cuda()[:, :L2], tpad.cuda()[:, :L2]
+    for (S, W, m, budget) in ((4, 256, 1024, 2048), (4, 256, 20000, 30000), (0, 100, 5, 9000)):
+        g = gpu_lib.select_verify_set(dv, tv, sink=S, window=W, top_m=m, budget=budget)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(g.cpu().numpy(), vo.select_verify_set(d, t, S, W, m, budget),
+                                      err_msg=str((S, W, m, budget)))
     say("case selector lognormal ragged")
     for L in (1, 31, 1025, 4099):
         d = rng.lognormal(0, 2, (2, L)).astype(np.float32)
