@@ -79,6 +79,9 @@ __device__ inline void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
+#ifndef VA_ROTATE
+#define VA_ROTATE 1   // per-head start offset of the context tile walk
+#endif
 #ifndef VA_TREE_FIRST
 #define VA_TREE_FIRST 1
 #endif
@@ -208,50 +211,6 @@ void partial_kernel(PartialParams p) {
     return (const T*)p.q + (int64_t)b * p.qs[0] + (int64_t)(kvh * p.G + g) * p.qs[1] + (int64_t)i * p.qs[2];
   };
 
-  // ---- bf16 queries of this row tile into LDS (row-major, chunk-swizzled)
-  if constexpr (BF) {
-    T* qs = (T*)qsm;
-    for (int c = tid; c < QROWS * CPR; c += kThreads) {
-      const int r = c / CPR, col = c % CPR;
-      u32x4 v = u32x4{0, 0, 0, 0};
-      if (row0 + r < p.R) v = *(const u32x4*)(q_row_ptr(row0 + r) + col * VEC);
-      *(u32x4*)(qs + r * D + swz<CPR>(r, col) * VEC) = v;
-    }
-  }
-
-  // ---- ancestor bitmasks of the draft tree, one per row of this tile.
-  // Ctx parts fill them with ones so the mask lookup needs no branch.
-  if (tree) {
-    for (int j = tid; j < p.N; j += kThreads) par[j] = p.parent[(int64_t)b * p.N + j];
-    for (int j = tid; j < 32 * RB * kAncWords; j += kThreads) (&anc[0][0])[j] = 0u;
-    __syncthreads();
-    if (tid < 32 * RB && row0 + tid < p.R) {
-      int j = (row0 + tid) % p.N;
-      for (int step = 0; step <= p.N && j >= 0; ++step) {
-        anc[tid][j >> 5] |= 1u << (j & 31);
-        int pj = par[j];
-        j = (pj >= -1 && pj < j) ? pj : -1;  // malformed parents end the path
-      }
-    }
-  } else {
-    for (int j = tid; j < 32 * RB * kAncWords; j += kThreads) (&anc[0][0])[j] = ~0u;
-  }
-  __syncthreads();
-
-  // ---- fp32 queries stay in registers as MFMA B operands (Q^T)
-  constexpr int QREG = BF ? 1 : D / 2;
-  float qf[RB][QREG];
-  if constexpr (!BF) {
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      const int r = row0 + 32 * rb + n;
-      const bool ok = r < p.R;
-      const T* qrow = q_row_ptr(ok ? r : 0);
-#pragma unroll
-      for (int ks = 0; ks < QREG; ++ks) qf[rb][ks] = ok ? qrow[2 * ks + h] : 0.f;
-    }
-  }
-
   // ---- key range of this part and its buffer resources
   const T* kbase;
   const T* vbase;
@@ -327,6 +286,20 @@ void partial_kernel(PartialParams p) {
     if constexpr (GATHER) return buf_load_i32(irs, (uint32_t)(kTileKeys * t + n) * 4u);
     return 0;
   };
+
+  // ---- fp32 queries stay in registers as MFMA B operands (Q^T)
+  constexpr int QREG = BF ? 1 : D / 2;
+  float qf[RB][QREG];
+  if constexpr (!BF) {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      const int r = row0 + 32 * rb + n;
+      const bool ok = r < p.R;
+      const T* qrow = q_row_ptr(ok ? r : 0);
+#pragma unroll
+      for (int ks = 0; ks < QREG; ++ks) qf[rb][ks] = ok ? qrow[2 * ks + h] : 0.f;
+    }
+  }
 
   // ---- online softmax state
   float m_run[RB], l_run[RB];
@@ -487,7 +460,20 @@ void partial_kernel(PartialParams p) {
   // after it.
   const int nw = tfirst < ntiles ? (ntiles - 1 - tfirst) / tstep + 1 : 0;   // tiles of this wavefront
   const int klast = nw > 0 ? nw - 1 : 0;
-  auto tile_of = [&](int k) __attribute__((always_inline)) -> int { return tfirst + (k < klast ? k : klast) * tstep; };
+  // A dense context part's last tile may be partial; it is taken last, with
+  // the mask.  The other tiles are walked starting at a per-head offset:
+  // the K/V regions of all heads lie a power of two apart, and heads walking
+  // them in step would crowd the same DRAM channels at the same time.
+  const bool partial_last = !tree && !gather && (ke % kTileKeys) != 0 && nw > 0 && tfirst + klast * tstep == ntiles - 1;
+  const int nrot = nw - (partial_last ? 1 : 0);
+  const int rot = VA_ROTATE && nrot > 0 ? (int)((int64_t)(b * p.Hkv + kvh) * nrot / ((int64_t)p.B * p.Hkv)) : 0;
+  auto tile_of = [&](int k) __attribute__((always_inline)) -> int {
+    if (k < nrot) {
+      const int kr = k + rot;
+      return tfirst + (kr >= nrot ? kr - nrot : kr) * tstep;
+    }
+    return tfirst + (k < klast ? k : klast) * tstep;
+  };
 #pragma unroll
   for (int pp = 0; pp < PF; ++pp) {
     const int ix = load_idx(tile_of(pp));
@@ -495,6 +481,39 @@ void partial_kernel(PartialParams p) {
     vmask[pp] = tile_mask(tile_of(pp), ix);
     ixr[pp] = load_idx(tile_of(pp + PF));
   }
+
+  // The queries and the tree mask are set up while the ring's first tiles
+  // are in flight.
+  // ---- bf16 queries of this row tile into LDS (row-major, chunk-swizzled)
+  if constexpr (BF) {
+    T* qs = (T*)qsm;
+    for (int c = tid; c < QROWS * CPR; c += kThreads) {
+      const int r = c / CPR, col = c % CPR;
+      u32x4 v = u32x4{0, 0, 0, 0};
+      if (row0 + r < p.R) v = *(const u32x4*)(q_row_ptr(row0 + r) + col * VEC);
+      *(u32x4*)(qs + r * D + swz<CPR>(r, col) * VEC) = v;
+    }
+  }
+
+  // ---- ancestor bitmasks of the draft tree, one per row of this tile.
+  // Ctx parts fill them with ones so the mask lookup needs no branch.
+  if (tree) {
+    for (int j = tid; j < p.N; j += kThreads) par[j] = p.parent[(int64_t)b * p.N + j];
+    for (int j = tid; j < 32 * RB * kAncWords; j += kThreads) (&anc[0][0])[j] = 0u;
+    __syncthreads();
+    if (tid < 32 * RB && row0 + tid < p.R) {
+      int j = (row0 + tid) % p.N;
+      for (int step = 0; step <= p.N && j >= 0; ++step) {
+        anc[tid][j >> 5] |= 1u << (j & 31);
+        int pj = par[j];
+        j = (pj >= -1 && pj < j) ? pj : -1;  // malformed parents end the path
+      }
+    }
+  } else {
+    for (int j = tid; j < 32 * RB * kAncWords; j += kThreads) (&anc[0][0])[j] = ~0u;
+  }
+  __syncthreads();
+
   // Stage ring slot pp in the wavefront's LDS tile; with reload, re-issue
   // each chunk for tile tn right after it is staged.
   auto stage = [&](int pp, bool reload, int tn) __attribute__((always_inline)) {
@@ -521,7 +540,10 @@ void partial_kernel(PartialParams p) {
         stage(pp, true, tn);
         vmask[pp] = tile_mask(tn, ixr[pp]);
         ixr[pp] = load_idx(tile_of(k + pp + 2 * PF));
-        compute(tfirst + (k + pp) * tstep, vm, masked_tag);
+        compute(tile_of(k + pp), vm, masked_tag);
+#ifdef VA_SLOT_FENCE
+        __builtin_amdgcn_sched_barrier(0);
+#endif
       }
     }
     return k;
@@ -529,8 +551,7 @@ void partial_kernel(PartialParams p) {
   int k;
   if (!tree && !gather) {
     // dense context: every tile but the part's last is whole (no mask)
-    const bool partial_last = (ke % kTileKeys) != 0 && nw > 0 && tfirst + (nw - 1) * tstep == ntiles - 1;
-    k = ring_loop(nw - (partial_last ? 1 : 0), std::false_type{});
+    k = ring_loop(nrot, std::false_type{});
   } else {
     k = ring_loop(nw, std::true_type{});
   }
@@ -539,7 +560,7 @@ void partial_kernel(PartialParams p) {
   for (int pp = 0; pp < PF; ++pp) {
     if (k + pp < nw) {
       stage(pp, false, 0);
-      compute(tfirst + (k + pp) * tstep, vmask[pp], std::true_type{});
+      compute(tile_of(k + pp), vmask[pp], std::true_type{});
     }
   }
 
@@ -719,8 +740,17 @@ void rows_kernel(PartialParams p) {
   u32x4 rg[RING][NCT];
   bool okr[RING];   // the thread's key exists (tile slot)
   int ixr[RING];    // gathered index of the thread's key in the tile the slot loads next
+  // Tile t of the part's walk.  Context tiles (all but a partial last one)
+  // start at a per-head offset, so heads do not read the same DRAM channels
+  // in step; past the end a slot re-fetches the last tile, never staged.
+  const int nrot = tree ? 0 : (gather ? ntiles : (ke - kb) / kTileKeys);
+  const int rot = VA_ROTATE && nrot > 0 ? (int)((int64_t)(b * p.Hkv + kvh) * nrot / ((int64_t)p.B * p.Hkv)) : 0;
   auto clamp_tile = [&](int t) __attribute__((always_inline)) -> int {
-    return t < ntiles ? t : (ntiles > 0 ? ntiles - 1 : 0);   // past the end: refetch, never staged
+    if (t < nrot) {
+      const int tr = t + rot;
+      return tr >= nrot ? tr - nrot : tr;
+    }
+    return t < ntiles ? t : (ntiles > 0 ? ntiles - 1 : 0);
   };
   auto load_idx = [&](int t) __attribute__((always_inline)) -> int {
     if constexpr (GATHER) return buf_load_i32(irs, (uint32_t)(kb + kTileKeys * clamp_tile(t) + kk_t) * 4u);
