@@ -161,6 +161,8 @@ def main():
     ap.add_argument("--copies", type=int, default=0, help="input copies rotated over steps (0: auto)")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-read-probe", action="store_true",
+                    help="skip the read-only HBM probe (counter-collection runs)")
     ap.add_argument("--copy-calib-gib", type=float, default=0.0,
                     help="after timing, run a plain device copy of this many GiB (HBM counter calibration)")
     args = ap.parse_args()
@@ -222,7 +224,7 @@ def main():
             ev[3].record()
 
     # achievable read bandwidth; this also brings the clock up before warm-up
-    read_peak = measured_read_peak(torch, dev)
+    read_peak = None if args.no_read_probe else measured_read_peak(torch, dev)
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
