@@ -75,8 +75,10 @@ va::Plan make_plan(const va_attn_desc* d, int32_t n_ctx) {
   const int G = d->Hq / d->Hkv;
   const int R = G * d->N;
   // bf16 with more than 64 query rows per KV head: the shared-tile rows
-  // kernel (256 rows per workgroup); otherwise 32 or 64 rows per workgroup.
-  pl.rb = (d->dtype == VA_BF16 && R > 64) ? va::kRowsKernel : (R <= 32 ? 1 : 2);
+  // kernel (256 rows per workgroup); other bf16 shapes: 32-row tiles (the
+  // row tiles of one split share that XCD's L2 and run in the same round,
+  // so K/V still come from HBM about once); fp32: 32 or 64 rows.
+  pl.rb = (d->dtype == VA_BF16 && R > 64) ? va::kRowsKernel : (d->dtype == VA_BF16 || R <= 32 ? 1 : 2);
   const int rows_per_tile = pl.rb == va::kRowsKernel ? 256 : 32 * pl.rb;
   pl.row_tiles = (R + rows_per_tile - 1) / rows_per_tile;
   const int64_t pairs = (int64_t)d->B * d->Hkv * pl.row_tiles;
@@ -92,7 +94,10 @@ va::Plan make_plan(const va_attn_desc* d, int32_t n_ctx) {
   if (want_splits < 1) want_splits = 1;
   int64_t len = n_ctx > 0 ? (n_ctx + want_splits - 1) / want_splits : 128;
   len = (len + 127) / 128 * 128;
-  if (len < 512) len = 512;
+#ifndef VA_MIN_SPLIT
+#define VA_MIN_SPLIT 512
+#endif
+  if (len < VA_MIN_SPLIT) len = VA_MIN_SPLIT;
   pl.split_len = (int)len;
   pl.n_ctx_splits = n_ctx > 0 ? (int)((n_ctx + len - 1) / len) : 0;
   pl.n_parts = pl.n_ctx_splits + 1;

@@ -150,14 +150,18 @@ __device__ inline int buf_load_i32(rsrc_t r, uint32_t off) {
 #ifndef VA_RING_TILES
 #define VA_RING_TILES 2
 #endif
-template <int RB, int ES, int D>
+template <int RB, int ES, int D, bool GATHER = false>
 struct KernelShape {
   // The HBM-bound shapes (bf16, one 32-row block) run one wavefront per SIMD
   // with a ring of register tiles in flight; registers are the larger
   // buffer on a CU (512 KiB vs 160 KiB of LDS).  D = 64 rows are half as
   // long, so a two-tile ring fits as well.
   static constexpr bool hbm_shape = RB == 1 && ES == 2;
-  static constexpr int prefetch = hbm_shape ? (D == 128 ? VA_RING_TILES : 2) : 1;
+  // The gathered (sparse) shape moves few bytes per workgroup and is bound
+  // by the latency of its index-then-row loads: two wavefronts per SIMD with
+  // one tile each in flight beat one wavefront with a two-tile ring.
+  static constexpr bool lat_shape = hbm_shape && GATHER;
+  static constexpr int prefetch = lat_shape ? 1 : (hbm_shape ? (D == 128 ? VA_RING_TILES : 2) : 1);
 #ifdef VA_HBM_WAVES_PER_EU
   static constexpr int waves_per_eu = hbm_shape ? VA_HBM_WAVES_PER_EU : 1;
 #else
@@ -167,11 +171,11 @@ struct KernelShape {
 
 template <class T, int D, int RB, bool GATHER>
 __global__ __launch_bounds__(kThreads)
-__attribute__((amdgpu_waves_per_eu(KernelShape<RB, sizeof(T), D>::waves_per_eu)))
+__attribute__((amdgpu_waves_per_eu(KernelShape<RB, sizeof(T), D, GATHER>::waves_per_eu)))
 void partial_kernel(PartialParams p) {
   constexpr int ES = sizeof(T);
   constexpr bool BF = ES == 2;
-  constexpr int PF = KernelShape<RB, ES, D>::prefetch;
+  constexpr int PF = KernelShape<RB, ES, D, GATHER>::prefetch;
   constexpr int VEC = 16 / ES;                     // elements per 16-byte chunk
   constexpr int CPR = D / VEC;                     // chunks per key row
   constexpr int NCH = kTileKeys * CPR / 64;        // chunks per lane per tile (K or V)
