@@ -15,6 +15,12 @@ the pages by eye:
   splits the two parts and re-joins them with a log-sum-exp merge; that merge
   is exact, so its result is the single softmax over the concatenated key set
   that is written out here.  No split, no merge, no blocking.
+* ``accept_commit`` is the last step of the verification workflow (Dustin,
+  "Workflow di Verifica" step 5): the accepted draft tokens are appended to
+  the cache and the rejected ones dropped.  The accepted tokens of a
+  sequence are a path of the draft tree from a root to its deepest accepted
+  node; their K/V rows are written, root first, at the sequence's current
+  cache length.
 * ``select_verify_set`` follows the selection rule of Dustin, "Metodologia"
   section 1 (Aggregazione Ibrida dell'Attenzione): protect an attention-sink
   prefix and a local window of recent tokens, then fill the remaining budget
@@ -227,3 +233,56 @@ def select_verify_set(draft_score: np.ndarray, target_score: np.ndarray,
     rows = [select_row(draft_score[b], target_score[b], sink, window, top_m, budget)
             for b in range(draft_score.shape[0])]
     return np.stack(rows) if rows else np.zeros((0, 0), dtype=np.int64)
+
+
+# ---------------------------------------------------------------------------
+# accept and commit
+
+
+def accepted_path(parent: Sequence[int], leaf: int) -> list:
+    """Draft nodes from the root down to ``leaf`` (empty when leaf == -1).
+
+    The accepted tokens of a speculative step form one root-to-node path of
+    the draft tree (a node is only accepted after its parent); the path is
+    read off the parent array, root first.
+    """
+    parent = [int(x) for x in parent]
+    if leaf == -1:
+        return []
+    if not 0 <= leaf < len(parent):
+        raise ValueError(f"accepted node {leaf} outside [-1, {len(parent)})")
+    path = []
+    j = leaf
+    while j != -1:
+        if not -1 <= parent[j] < j:
+            raise ValueError(f"parent[{j}] = {parent[j]} breaks -1 <= parent[i] < i")
+        path.append(j)
+        j = parent[j]
+    return path[::-1]
+
+
+def accept_commit(k_cache: np.ndarray, v_cache: np.ndarray, k_draft: np.ndarray, v_draft: np.ndarray,
+                  parent: np.ndarray, accepted: Sequence[int], cache_len: Sequence[int]):
+    """Append each sequence's accepted draft path to its cache (Dustin,
+    "Workflow di Verifica" step 5).
+
+    k_cache/v_cache [B, Hkv, capacity, D] hold cache_len[b] valid tokens of
+    sequence b; the K/V rows of the accepted path's nodes (all KV heads) go
+    to positions cache_len[b], cache_len[b] + 1, ... in root-to-leaf order.
+    Rows that would land at or past the capacity are dropped.  Returns new
+    copies of the caches and new_len[b] = cache_len[b] + path length.
+    Element values are copied bit for bit (any dtype).
+    """
+    kc = np.array(k_cache, copy=True)
+    vc = np.array(v_cache, copy=True)
+    capacity = kc.shape[2]
+    new_len = np.array(cache_len, dtype=np.int64).copy()
+    for b in range(kc.shape[0]):
+        path = accepted_path(parent[b], int(accepted[b]))
+        for depth, node in enumerate(path):
+            pos = int(cache_len[b]) + depth
+            if pos < capacity:
+                kc[b, :, pos, :] = k_draft[b, :, node, :]
+                vc[b, :, pos, :] = v_draft[b, :, node, :]
+        new_len[b] = int(cache_len[b]) + len(path)
+    return kc, vc, new_len

@@ -506,3 +506,79 @@ def test_selector_config4_budget_split():
     x = synth.make_inputs(cfg)
     idx = vo.select_verify_set(x.draft_score, x.target_score, cfg.sink, cfg.window, cfg.top_m, cfg.budget)
     assert idx.shape == (2, cfg.budget)
+
+
+# ---------------------------------------------------------------------------
+# accept and commit (Dustin, "Workflow di Verifica" step 5)
+
+
+def test_accepted_path_matches_hand_tree():
+    # the hand-derived fixture lists, per node, the draft nodes on its path
+    # back to the context (ascending = root first in a topological tree)
+    g = json.load(open(os.path.join(GOLDEN, "tree_hand_example.json")))
+    for leaf, visible in enumerate(g["visible"]):
+        assert vo.accepted_path(g["parent"], leaf) == visible
+    assert vo.accepted_path(g["parent"], -1) == []
+
+
+def _commit_inputs(rng, B=3, Hkv=2, cap=40, N=9, D=8, dtype=np.uint16):
+    if dtype == np.uint16:
+        draw = lambda *shape: rng.integers(0, 1 << 16, shape, dtype=np.uint16)
+    else:
+        draw = lambda *shape: rng.standard_normal(shape).astype(np.float32)
+    return draw(B, Hkv, cap, D), draw(B, Hkv, cap, D), draw(B, Hkv, N, D), draw(B, Hkv, N, D)
+
+
+def test_commit_chain_is_a_slice_copy():
+    rng = np.random.default_rng(5)
+    kc, vc, kd, vd = _commit_inputs(rng)
+    B, N = kd.shape[0], kd.shape[2]
+    parent = np.tile(np.arange(-1, N - 1, dtype=np.int32), (B, 1))
+    accepted = np.array([4, 0, N - 1])
+    cache_len = np.array([10, 0, 31])
+    nk, nv, new_len = vo.accept_commit(kc, vc, kd, vd, parent, accepted, cache_len)
+    np.testing.assert_array_equal(new_len, cache_len + accepted + 1)
+    for b in range(B):
+        n = accepted[b] + 1
+        L0 = cache_len[b]
+        np.testing.assert_array_equal(nk[b, :, L0:L0 + n], kd[b, :, :n])
+        np.testing.assert_array_equal(nv[b, :, L0:L0 + n], vd[b, :, :n])
+        np.testing.assert_array_equal(nk[b, :, :L0], kc[b, :, :L0])
+        np.testing.assert_array_equal(nk[b, :, L0 + n:], kc[b, :, L0 + n:])
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_commit_random_tree_rows_are_the_ancestors(seed):
+    rng = np.random.default_rng(seed)
+    kc, vc, kd, vd = _commit_inputs(rng, dtype=np.float32 if seed == 1 else np.uint16)
+    B, N = kd.shape[0], kd.shape[2]
+    parent = np.stack([synth.uniform_parents(rng, N) for _ in range(B)]).astype(np.int32)
+    accepted = rng.integers(-1, N, B)
+    cache_len = rng.integers(0, 30, B)
+    nk, nv, new_len = vo.accept_commit(kc, vc, kd, vd, parent, accepted, cache_len)
+    for b in range(B):
+        # the committed nodes are the accepted node and its ancestors, in
+        # index order (the independent ancestor-mask construction)
+        nodes = np.nonzero(vo.ancestor_mask(parent[b])[accepted[b]])[0] if accepted[b] >= 0 else np.zeros(0, int)
+        assert new_len[b] == cache_len[b] + nodes.size
+        for d, node in enumerate(nodes):
+            np.testing.assert_array_equal(nk[b, :, cache_len[b] + d], kd[b, :, node])
+            np.testing.assert_array_equal(nv[b, :, cache_len[b] + d], vd[b, :, node])
+        untouched = np.r_[0:cache_len[b], cache_len[b] + nodes.size:kc.shape[2]]
+        np.testing.assert_array_equal(nk[b][:, untouched], kc[b][:, untouched])
+        np.testing.assert_array_equal(nv[b][:, untouched], vc[b][:, untouched])
+
+
+def test_commit_nothing_accepted_and_capacity():
+    rng = np.random.default_rng(9)
+    kc, vc, kd, vd = _commit_inputs(rng, B=2, cap=12, N=6)
+    parent = np.tile(np.arange(-1, 5, dtype=np.int32), (2, 1))
+    nk, nv, new_len = vo.accept_commit(kc, vc, kd, vd, parent, [-1, 5], [3, 9])
+    np.testing.assert_array_equal(nk[0], kc[0])
+    np.testing.assert_array_equal(nv[0], vc[0])
+    assert list(new_len) == [3, 15]
+    # only positions 9, 10, 11 exist: nodes 0..2 land, 3..5 are dropped
+    np.testing.assert_array_equal(nk[1, :, 9:12], kd[1, :, 0:3])
+    np.testing.assert_array_equal(nk[1, :, :9], kc[1, :, :9])
+    with pytest.raises(ValueError):
+        vo.accept_commit(kc, vc, kd, vd, parent, [6, -1], [0, 0])
