@@ -152,6 +152,39 @@ def cpu_baseline(cfg, x, budget_s: float):
     }
 
 
+def measure_commit(torch, ops, cfg, x, base, dev, reps: int = 20):
+    """Accept-and-commit of the deepest draft node of every sequence (its
+    whole root path) into the last rows of the benchmarked cache; mean of
+    `reps` launches timed with HIP events on the launching stream.  Runs
+    after the timed steps (it overwrites cache rows)."""
+    depth = np.zeros((cfg.B, cfg.N), dtype=np.int64)
+    for b in range(cfg.B):
+        for i in range(cfg.N):
+            p = int(x.parent[b, i])
+            depth[b, i] = 1 if p < 0 else depth[b, p] + 1
+    leaf = depth.argmax(axis=1)
+    plen = depth.max(axis=1)
+    accepted = torch.from_numpy(leaf.astype(np.int32)).to(dev)
+    cache_len = torch.from_numpy((cfg.L - plen).astype(np.int32)).to(dev)
+    new_len = torch.empty(cfg.B, dtype=torch.int32, device=dev)
+    args = (base["k_cache"], base["v_cache"], base["k_draft"], base["v_draft"], base["parent"], accepted, cache_len,
+            new_len)
+    desc = ops.make_commit_desc(*args[:4])
+    ops.accept_commit(*args)
+    torch.cuda.synchronize()
+    a, bev = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        ops.accept_commit(*args, desc=desc)
+    bev.record()
+    bev.synchronize()
+    us = a.elapsed_time(bev) * 1e3 / reps
+    e = 4 if cfg.dtype == "fp32" else 2
+    nbytes = int(2 * 2 * cfg.Hkv * cfg.D * e * int(plen.sum()))   # K and V rows, read once and written once
+    return {"us": round(us, 2), "bytes": nbytes, "gbs": round(nbytes / (us * 1e-6) / 1e9, 2),
+            "rows_per_sequence": int(plen.max()), "kernel": "commit_kernel"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -312,6 +345,7 @@ def main():
         "roofline": roof,
     }
     roof["traffic"], roof["traffic_source"] = committed_traffic(kernel, cfg.name)
+    line["accept_commit"] = measure_commit(torch, ops, cfg, x, base, dev)
     if args.copy_calib_gib > 0:
         n = int(args.copy_calib_gib * (1 << 30))
         src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)

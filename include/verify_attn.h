@@ -156,6 +156,29 @@ va_status verify_attn_merge(const va_attn_desc* desc, int32_t n_ctx,
                             void* out, float* lse,
                             const void* ws, size_t ws_bytes, void* stream);
 
+/* Accept and commit (Dustin, "Workflow di Verifica" step 5: accepted draft
+ * tokens are appended to the cache, rejected ones dropped).  The accepted
+ * tokens of sequence b are the root-to-node path of the draft tree that ends
+ * at node accepted[b]; their K/V rows (every KV head) are copied, root
+ * first, from k_draft / v_draft to positions cache_len[b], cache_len[b] + 1,
+ * ... of k_cache / v_cache, and new_len[b] = cache_len[b] + path length.
+ *   desc        as for verify_attn_dense, with desc->L = the cache capacity
+ *               (token rows allocated per (sequence, kv head)); q / out
+ *               fields are not used
+ *   k_cache, v_cache  [B, Hkv, capacity, D], written in place
+ *   parent      [B, N] as for verify_attn_dense
+ *   accepted    [B] int32 device: deepest accepted node in [0, N), or -1 for
+ *               none (values outside [-1, N) act as -1)
+ *   cache_len   [B] int32 device: valid tokens per sequence before the call
+ *   new_len     [B] int32 device, written
+ * Rows that would land at or past the capacity are not written (new_len
+ * still counts them).  Device pointers, asynchronous on `stream`; no
+ * workspace.  Malformed parents end a path as in the tree mask. */
+va_status accept_commit(const va_attn_desc* desc, void* k_cache, void* v_cache,
+                        const void* k_draft, const void* v_draft, const int32_t* parent,
+                        const int32_t* accepted, const int32_t* cache_len, int32_t* new_len,
+                        void* stream);
+
 /* Workspace bytes needed by select_verify_set for B rows of L scores. */
 va_status va_select_workspace_size(int32_t B, int32_t L, size_t* bytes);
 

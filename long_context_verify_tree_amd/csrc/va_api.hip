@@ -282,6 +282,42 @@ va_status select_verify_set(const float* draft_score, const float* target_score,
   return ok();
 }
 
+va_status accept_commit(const va_attn_desc* desc, void* k_cache, void* v_cache, const void* k_draft,
+                        const void* v_draft, const int32_t* parent, const int32_t* accepted, const int32_t* cache_len,
+                        int32_t* new_len, void* stream) {
+  va_status st = check_desc(desc);
+  if (st != VA_OK) return st;
+  if (!k_cache || !v_cache || !k_draft || !v_draft || !parent || !accepted || !cache_len || !new_len)
+    return fail(VA_EINVAL, "every tensor of accept_commit must be non-NULL");
+  if (misaligned(k_cache) || misaligned(v_cache) || misaligned(k_draft) || misaligned(v_draft))
+    return fail(VA_EINVAL, "tensor base pointers must be 16-byte aligned");
+  va::CommitParams p{};
+  p.kc = k_cache;
+  p.vc = v_cache;
+  p.kd = k_draft;
+  p.vd = v_draft;
+  p.parent = parent;
+  p.accepted = accepted;
+  p.cache_len = cache_len;
+  p.new_len = new_len;
+  for (int a = 0; a < 3; ++a) {
+    p.kcs[a] = desc->kc_stride[a];
+    p.vcs[a] = desc->vc_stride[a];
+    p.kds[a] = desc->kd_stride[a];
+    p.vds[a] = desc->vd_stride[a];
+  }
+  p.B = desc->B;
+  p.Hkv = desc->Hkv;
+  p.N = desc->N;
+  p.capacity = desc->L;
+  p.es = desc->dtype == VA_BF16 ? 2 : 4;
+  p.row_bytes = desc->D * p.es;
+  if ((int64_t)p.B * p.Hkv > 0x7fffffff) return fail(VA_EUNSUPPORTED, "problem too large for one launch");
+  hipError_t e = va::launch_commit(p, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(VA_EHIP, "commit kernel launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
 const char* va_status_str(va_status s) {
   switch (s) {
     case VA_OK: return "ok";

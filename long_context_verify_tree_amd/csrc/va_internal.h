@@ -61,7 +61,21 @@ struct MergeParams {
   int Hq, N, n_parts;
 };
 
-// Launchers (defined in va_attn.hip).  Return the hipError_t of the launch.
+struct CommitParams {
+  void* kc;
+  void* vc;
+  const void* kd;
+  const void* vd;
+  const int32_t* parent;
+  const int32_t* accepted;
+  const int32_t* cache_len;
+  int32_t* new_len;
+  int64_t kcs[3], vcs[3], kds[3], vds[3];
+  int B, Hkv, N, capacity, es, row_bytes;
+};
+
+// Launchers (va_attn.hip, va_commit.hip).  Return the hipError_t of the launch.
+hipError_t launch_commit(const CommitParams& p, hipStream_t stream);
 hipError_t launch_partials(const PartialParams& p, int dtype, int D, int rb, bool gather,
                            hipStream_t stream);
 hipError_t launch_merge(const MergeParams& p, int dtype, int D, hipStream_t stream);

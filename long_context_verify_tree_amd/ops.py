@@ -58,6 +58,7 @@ def _declare(lib):
         "verify_attn_merge": (i32, [_DESC_P, i32, _P, _P, _P, sz, _P]),
         "va_select_workspace_size": (i32, [i32, i32, ctypes.POINTER(sz)]),
         "select_verify_set": (i32, [_P, _P, i32, i32, i64, i32, i32, i32, i32, _P, _P, sz, _P]),
+        "accept_commit": (i32, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
         "va_status_str": (ctypes.c_char_p, [i32]),
         "va_last_error": (ctypes.c_char_p, []),
         "va_version": (i32, []),
@@ -249,3 +250,48 @@ def select_verify_set(draft_score, target_score, *, sink: int, window: int, top_
                                   workspace.numel() if workspace is not None else 0,
                                   _stream(draft_score.device)))
     return out
+
+
+def make_commit_desc(k_cache, v_cache, k_draft, v_draft) -> AttnDesc:
+    """Descriptor for accept_commit: caches [B, Hkv, capacity, D], drafts
+    [B, Hkv, N, D] (desc.L = capacity; query/output fields unused)."""
+    if k_cache.dtype != k_draft.dtype or v_cache.dtype != k_draft.dtype or v_draft.dtype != k_draft.dtype:
+        raise ValueError("caches and drafts must share a dtype")
+    B, Hkv, N, D = k_draft.shape
+    if k_cache.shape[:2] != (B, Hkv) or k_cache.shape[3] != D or v_cache.shape != k_cache.shape:
+        raise ValueError("k_cache / v_cache must be [B, Hkv, capacity, D]")
+    d = AttnDesc()
+    d.B, d.Hq, d.Hkv, d.D, d.L, d.N = B, Hkv, Hkv, D, k_cache.shape[2], N
+    d.dtype = _dtype_code(k_cache)
+    d.scale = 0.0
+    zero = (ctypes.c_int64 * 3)(0, 0, 0)
+    d.q_stride = zero
+    d.o_stride = zero
+    d.kc_stride = _strides3(k_cache)
+    d.vc_stride = _strides3(v_cache)
+    d.kd_stride = _strides3(k_draft)
+    d.vd_stride = _strides3(v_draft)
+    return d
+
+
+def accept_commit(k_cache, v_cache, k_draft, v_draft, parent, accepted, cache_len, new_len=None,
+                  desc: Optional[AttnDesc] = None) -> torch.Tensor:
+    """Append each sequence's accepted draft path to its cache in place.
+
+    k_cache/v_cache [B, Hkv, capacity, D]; accepted/cache_len int32 [B].
+    Returns new_len int32 [B] (cache_len + path length).  `desc` (from
+    make_commit_desc for the same tensors) skips rebuilding the descriptor."""
+    load()
+    if desc is None:
+        desc = make_commit_desc(k_cache, v_cache, k_draft, v_draft)
+        B, N = desc.B, desc.N
+        for t, name in ((parent, "parent"), (accepted, "accepted"), (cache_len, "cache_len")):
+            if t.dtype != torch.int32 or not t.is_contiguous():
+                raise ValueError(f"{name} must be contiguous int32")
+        if parent.shape != (B, N) or accepted.shape != (B,) or cache_len.shape != (B,):
+            raise ValueError("parent [B, N], accepted [B] and cache_len [B] expected")
+    if new_len is None:
+        new_len = torch.empty(desc.B, dtype=torch.int32, device=k_cache.device)
+    _check(_lib.accept_commit(ctypes.byref(desc), _ptr(k_cache), _ptr(v_cache), _ptr(k_draft), _ptr(v_draft),
+                              _ptr(parent), _ptr(accepted), _ptr(cache_len), _ptr(new_len), _stream(k_cache.device)))
+    return new_len

@@ -173,3 +173,19 @@ def test_product_path_does_not_touch_the_oracle():
                 bad = re.findall(r"^\s*(?:import\s+oracle|from\s+oracle|#\s*include\s*[<\"].*oracle)", text,
                                  flags=re.M)
                 assert not bad, (os.path.join(dirpath, f), bad)
+
+
+def test_commit_rejects_before_launch(ops):
+    d = good_desc(ops)
+    f = ops._lib.accept_commit
+    args = [FAKE] * 8
+    assert f(None, *args, None) == ops.VA_EINVAL
+    for k in range(8):
+        a = list(args)
+        a[k] = None
+        assert f(ctypes.byref(d), *a, None) == ops.VA_EINVAL, k
+    a = list(args)
+    a[0] = ctypes.c_void_p(0x100004)   # misaligned cache
+    assert f(ctypes.byref(d), *a, None) == ops.VA_EINVAL
+    d.D = 96
+    assert f(ctypes.byref(d), *args, None) == ops.VA_EUNSUPPORTED
