@@ -21,6 +21,13 @@ the pages by eye:
   sequence are a path of the draft tree from a root to its deepest accepted
   node; their K/V rows are written, root first, at the sequence's current
   cache length.
+* ``importance_scores`` produces the per-token scores the selector ranks
+  (Dustin, "Metodologia" sections 1-2: attention scores of the target's
+  previous passes and of the draft's lookahead, computed on a few selected
+  heads only, aggregated into one global importance map).  The pages do not
+  spell the aggregation out; the plain reading taken here is the sum, over
+  the scoring heads and their query rows, of the attention probabilities
+  each row gives to every context token.
 * ``select_verify_set`` follows the selection rule of Dustin, "Metodologia"
   section 1 (Aggregazione Ibrida dell'Attenzione): protect an attention-sink
   prefix and a local window of recent tokens, then fill the remaining budget
@@ -39,7 +46,9 @@ design notes of the repository):
   union; the draft tier takes min(m, remaining budget, remaining tokens);
 * ties in a score go to the lower token index; NaN ranks below -inf, and
   -0 equals +0; the output index list is ascending;
-* ``lse`` is the natural-log log-sum-exp of the scaled scores of a row.
+* ``lse`` is the natural-log log-sum-exp of the scaled scores of a row;
+* importance scores: the softmax of a scoring row runs over the context
+  tokens [0, L) only, and the map is the plain sum of the probabilities.
 
 Parity status: every function here is pinned by the ``-m "not gpu"`` tests
 (closed forms, textbook special cases, brute force); none is "parity
@@ -286,3 +295,32 @@ def accept_commit(k_cache: np.ndarray, v_cache: np.ndarray, k_draft: np.ndarray,
                 vc[b, :, pos, :] = v_draft[b, :, node, :]
         new_len[b] = int(cache_len[b]) + len(path)
     return kc, vc, new_len
+
+
+# ---------------------------------------------------------------------------
+# importance scores
+
+
+def importance_scores(q: np.ndarray, k: np.ndarray, scale: Optional[float] = None) -> np.ndarray:
+    """Global importance map [B, L] from a few scoring heads (Dustin,
+    "Metodologia" sections 1-2).
+
+    q [B, Hs, M, D]: the query rows of the scoring heads (draft lookahead
+    rows, or the target's previous rows); k [B, Hs, L, D]: the context keys
+    each scoring head reads.  score[b, j] = sum over h < Hs and i < M of
+    softmax_j(scale * <q[b, h, i], k[b, h, j]>), the softmax taken over the
+    L context tokens.
+    """
+    qf, kf = as_f64(q), as_f64(k)
+    B, Hs, M, D = qf.shape
+    L = kf.shape[2]
+    if scale is None or scale <= 0:
+        scale = default_scale(D)
+    out = np.zeros((B, L), dtype=np.float64)
+    for b in range(B):
+        for h in range(Hs):
+            s = scale * (qf[b, h] @ kf[b, h].T)              # [M, L]
+            s = s - s.max(axis=1, keepdims=True)
+            p = np.exp(s)
+            out[b] += (p / p.sum(axis=1, keepdims=True)).sum(axis=0)
+    return out

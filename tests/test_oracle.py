@@ -582,3 +582,57 @@ def test_commit_nothing_accepted_and_capacity():
     np.testing.assert_array_equal(nk[1, :, :9], kc[1, :, :9])
     with pytest.raises(ValueError):
         vo.accept_commit(kc, vc, kd, vd, parent, [6, -1], [0, 0])
+
+
+# ---------------------------------------------------------------------------
+# importance scores (Dustin, "Metodologia" sections 1-2)
+
+
+def test_scores_single_row_is_scipy_softmax():
+    from scipy.special import softmax
+    rng = np.random.default_rng(21)
+    q = rng.standard_normal((1, 1, 1, 16)).astype(np.float32)
+    k = rng.standard_normal((1, 1, 50, 16)).astype(np.float32)
+    got = vo.importance_scores(q, k, scale=0.3)
+    want = softmax(0.3 * (k[0, 0].astype(np.float64) @ q[0, 0, 0].astype(np.float64)))
+    np.testing.assert_allclose(got[0], want, rtol=1e-12, atol=0)
+
+
+def test_scores_equal_keys_are_uniform_and_rows_sum_to_one():
+    rng = np.random.default_rng(22)
+    B, Hs, M, L, D = 2, 3, 5, 37, 8
+    q = rng.standard_normal((B, Hs, M, D)).astype(np.float32)
+    k = np.tile(rng.standard_normal((B, Hs, 1, D)).astype(np.float32), (1, 1, L, 1))
+    np.testing.assert_allclose(vo.importance_scores(q, k), Hs * M / L, rtol=1e-12)
+    k2 = rng.standard_normal((B, Hs, L, D)).astype(np.float32)
+    s = vo.importance_scores(q, k2)
+    np.testing.assert_allclose(s.sum(axis=1), Hs * M, rtol=1e-12)    # every row's probabilities sum to 1
+    assert (s > 0).all()
+
+
+def test_scores_two_keys_closed_form_and_head_sum():
+    # one query, two keys: p_0 = 1 / (1 + exp(scale * (s1 - s0)))
+    q = np.array([[[[1.0, 2.0]]]], dtype=np.float32)
+    k = np.array([[[[0.5, 0.0], [0.0, 1.0]]]], dtype=np.float32)   # s0 = 0.5, s1 = 2
+    got = vo.importance_scores(q, k, scale=1.0)
+    p0 = 1.0 / (1.0 + math.exp(2.0 - 0.5))
+    np.testing.assert_allclose(got[0], [p0, 1 - p0], rtol=1e-14)
+    # two heads: the map is the sum of the per-head maps
+    q2 = np.concatenate([q, 2 * q], axis=1)
+    k2 = np.concatenate([k, k[:, :, ::-1]], axis=1)
+    s_a = vo.importance_scores(q, k, scale=1.0)
+    s_b = vo.importance_scores(2 * q, k[:, :, ::-1], scale=1.0)
+    np.testing.assert_allclose(vo.importance_scores(q2, k2, scale=1.0), s_a + s_b, rtol=1e-14)
+
+
+def test_scores_bf16_bits_and_default_scale():
+    rng = np.random.default_rng(23)
+    q32 = rng.standard_normal((1, 2, 3, 64)).astype(np.float32)
+    k32 = rng.standard_normal((1, 2, 40, 64)).astype(np.float32)
+    qb, kb = synth.f32_to_bf16_bits(q32), synth.f32_to_bf16_bits(k32)
+    # bf16 bits are read exactly: the same map as the float32 inputs rounded to bf16
+    np.testing.assert_allclose(vo.importance_scores(qb, kb),
+                               vo.importance_scores(vo.bf16_bits_to_f64(qb).astype(np.float32),
+                                                    vo.bf16_bits_to_f64(kb).astype(np.float32)), rtol=1e-12)
+    np.testing.assert_allclose(vo.importance_scores(q32, k32), vo.importance_scores(q32, k32, scale=1 / 8.0),
+                               rtol=1e-14)
