@@ -185,6 +185,38 @@ def measure_commit(torch, ops, cfg, x, base, dev, reps: int = 20):
             "rows_per_sequence": int(plen.max()), "kernel": "commit_kernel"}
 
 
+SCORE_HEADS = 2   # scoring heads of the importance map (a few selected heads)
+
+
+def measure_scores(torch, ops, cfg, base, dev, step_ms, reps: int = 20):
+    """Importance map of SCORE_HEADS scoring heads with the N draft rows
+    each, over the benchmarked cache's first KV heads; mean of `reps` calls
+    timed with HIP events on the launching stream."""
+    if cfg.dtype != "bf16" or cfg.L == 0:
+        return None
+    hs = min(SCORE_HEADS, cfg.Hkv)
+    q = base["q"][:, :hs]
+    k = base["k_cache"][:, :hs]
+    desc = ops.make_score_desc(q, k)
+    ws = torch.empty(ops.scores_workspace_size(desc), dtype=torch.uint8, device=dev)
+    out = torch.empty(cfg.B, cfg.L, dtype=torch.float32, device=dev)
+    ops.importance_scores(q, k, out=out, workspace=ws, desc=desc)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        ops.importance_scores(q, k, out=out, workspace=ws, desc=desc)
+    b.record()
+    b.synchronize()
+    us = a.elapsed_time(b) * 1e3 / reps
+    nbytes = cfg.B * hs * (cfg.L + cfg.N) * cfg.D * 2 + cfg.B * cfg.L * 4   # K and q read, map written
+    return {"us": round(us, 2), "bytes": nbytes, "gbs": round(nbytes / (us * 1e-6) / 1e9, 1),
+            "frac_of_hbm_peak": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+            "scoring_heads": hs, "rows_per_head": cfg.N,
+            "vs_one_verification_step": round(us * 1e-3 / step_ms, 4),
+            "kernels": ["score_partial_kernel", "score_finish_kernel"]}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -346,6 +378,7 @@ def main():
     }
     roof["traffic"], roof["traffic_source"] = committed_traffic(kernel, cfg.name)
     line["accept_commit"] = measure_commit(torch, ops, cfg, x, base, dev)
+    line["importance_scores"] = measure_scores(torch, ops, cfg, base, dev, ms_per_step)
     if args.copy_calib_gib > 0:
         n = int(args.copy_calib_gib * (1 << 30))
         src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)

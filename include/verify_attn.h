@@ -156,6 +156,39 @@ va_status verify_attn_merge(const va_attn_desc* desc, int32_t n_ctx,
                             void* out, float* lse,
                             const void* ws, size_t ws_bytes, void* stream);
 
+/* Importance scores for the selector (Dustin, "Metodologia" sections 1-2:
+ * attention scores of a few scoring heads -- the draft's lookahead rows or
+ * the target's previous rows -- aggregated into one global importance map):
+ *
+ *     score[b, j] = sum_{h < Hs} sum_{i < M} softmax_j(scale * <q[b,h,i], k[b,h,j]>)
+ *
+ * with the softmax over the L context tokens (the pages leave the
+ * aggregation open; the plain reading is this sum of probabilities).  The
+ * result is what select_verify_set takes as draft_score or target_score. */
+typedef struct {
+  int32_t B;            /* sequences                                          */
+  int32_t Hs;           /* scoring heads                                      */
+  int32_t M;            /* query rows per scoring head, 1..32                 */
+  int32_t D;            /* head dimension, 64 or 128                          */
+  int32_t L;            /* context tokens, >= 0                               */
+  int32_t dtype;        /* VA_BF16 only                                       */
+  float scale;          /* softmax scale; <= 0 selects 1/sqrt(D)              */
+  int64_t q_stride[3];  /* q [B, Hs, M, D] over (b, head, row), unit D stride */
+  int64_t k_stride[3];  /* k [B, Hs, L, D] over (b, head, token); token stride
+                           > 0, (L + 64) x token stride x 2 bytes <= 2 GiB    */
+} va_score_desc;
+
+/* Workspace bytes importance_scores needs for this desc (about
+ * 4 x B x Hs x M x L bytes: the scaled scores between its two kernels). */
+va_status va_scores_workspace_size(const va_score_desc* desc, size_t* bytes);
+
+/* score [B, L] float32 device, row stride ld_score (>= L), written.  q and
+ * k device pointers, 16-byte aligned; ws device workspace of
+ * va_scores_workspace_size bytes.  Two kernels on `stream`. */
+va_status importance_scores(const va_score_desc* desc, const void* q, const void* k,
+                            float* score, int64_t ld_score,
+                            void* ws, size_t ws_bytes, void* stream);
+
 /* Accept and commit (Dustin, "Workflow di Verifica" step 5: accepted draft
  * tokens are appended to the cache, rejected ones dropped).  The accepted
  * tokens of sequence b are the root-to-node path of the draft tree that ends

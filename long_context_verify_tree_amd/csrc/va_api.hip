@@ -318,6 +318,102 @@ va_status accept_commit(const va_attn_desc* desc, void* k_cache, void* v_cache, 
   return ok();
 }
 
+namespace {
+
+struct ScorePlan {
+  int split_len, n_splits;
+  int64_t ld_s;
+  size_t off_m, off_l, ws_bytes;
+};
+
+va_status check_score_desc(const va_score_desc* d) {
+  if (d == nullptr) return fail(VA_EINVAL, "desc is NULL");
+  if (d->B < 1 || d->Hs < 1) return fail(VA_EINVAL, "B and Hs must be >= 1");
+  if (d->L < 0) return fail(VA_EINVAL, "L must be >= 0");
+  if (d->M < 1 || d->M > 32) return fail(VA_EUNSUPPORTED, "M = %d query rows per head (supported: 1..32)", d->M);
+  if (d->D != 64 && d->D != 128) return fail(VA_EUNSUPPORTED, "D = %d (supported: 64, 128)", d->D);
+  if (d->dtype != VA_BF16) return fail(VA_EUNSUPPORTED, "importance scores take bf16 queries and keys");
+  if (isnan(d->scale) || isinf(d->scale)) return fail(VA_EINVAL, "scale must be finite");
+  for (int a = 0; a < 3; ++a)
+    if (d->q_stride[a] % 8 != 0 || d->k_stride[a] % 8 != 0)
+      return fail(VA_EINVAL, "q / k strides must keep rows 16-byte aligned");
+  if (d->k_stride[2] <= 0) return fail(VA_EUNSUPPORTED, "k token stride must be positive");
+  if (((int64_t)d->L + 64) * d->k_stride[2] * 2 > ((int64_t)1 << 31))
+    return fail(VA_EUNSUPPORTED, "k: the keys of one (sequence, head) exceed the 2 GiB region limit");
+  return VA_OK;
+}
+
+ScorePlan make_score_plan(const va_score_desc* d) {
+  ScorePlan pl{};
+  const int64_t pairs = (int64_t)d->B * d->Hs;
+#ifndef VA_SCORE_GROUPS
+#define VA_SCORE_GROUPS 256
+#endif
+  int64_t want = (VA_SCORE_GROUPS + pairs - 1) / pairs;
+  if (want < 1) want = 1;
+  int64_t len = d->L > 0 ? (d->L + want - 1) / want : 32;
+  len = (len + 31) / 32 * 32;
+  if (len < 512) len = 512;
+  pl.split_len = (int)len;
+  pl.n_splits = d->L > 0 ? (int)((d->L + len - 1) / len) : 0;
+  pl.ld_s = ((int64_t)d->L + 31) / 32 * 32;
+  const int64_t rows = (int64_t)d->B * d->Hs * d->M;
+  pl.off_m = align_up((size_t)rows * pl.ld_s * sizeof(float));
+  pl.off_l = pl.off_m + align_up((size_t)rows * pl.n_splits * sizeof(float));
+  pl.ws_bytes = pl.off_l + align_up((size_t)rows * pl.n_splits * sizeof(float));
+  return pl;
+}
+
+}  // namespace
+
+va_status va_scores_workspace_size(const va_score_desc* desc, size_t* bytes) {
+  va_status st = check_score_desc(desc);
+  if (st != VA_OK) return st;
+  if (bytes == nullptr) return fail(VA_EINVAL, "bytes is NULL");
+  *bytes = make_score_plan(desc).ws_bytes;
+  return ok();
+}
+
+va_status importance_scores(const va_score_desc* desc, const void* q, const void* k, float* score, int64_t ld_score,
+                            void* ws, size_t ws_bytes, void* stream) {
+  va_status st = check_score_desc(desc);
+  if (st != VA_OK) return st;
+  if (!q || !score || (desc->L > 0 && !k)) return fail(VA_EINVAL, "q, k and score must be non-NULL");
+  if (misaligned(q) || misaligned(k)) return fail(VA_EINVAL, "q and k must be 16-byte aligned");
+  if (ld_score < desc->L) return fail(VA_EINVAL, "ld_score (%lld) < L (%d)", (long long)ld_score, desc->L);
+  const ScorePlan pl = make_score_plan(desc);
+  if (ws == nullptr || ws_bytes < pl.ws_bytes)
+    return fail(VA_EWORKSPACE, "workspace of %zu bytes needed, %zu given", pl.ws_bytes, ws ? ws_bytes : (size_t)0);
+  if (desc->L == 0) return ok();
+  const int64_t groups = (int64_t)desc->B * desc->Hs * pl.n_splits;
+  if (groups > 0x7fffffff) return fail(VA_EUNSUPPORTED, "problem too large for one launch");
+  va::ScoreParams p{};
+  p.q = q;
+  p.k = k;
+  for (int a = 0; a < 3; ++a) {
+    p.qs[a] = desc->q_stride[a];
+    p.ks[a] = desc->k_stride[a];
+  }
+  p.score = score;
+  p.ld_out = ld_score;
+  p.s = (float*)ws;
+  p.stat_m = (float*)((char*)ws + pl.off_m);
+  p.stat_l = (float*)((char*)ws + pl.off_l);
+  p.ld_s = pl.ld_s;
+  p.B = desc->B;
+  p.Hs = desc->Hs;
+  p.M = desc->M;
+  p.L = desc->L;
+  p.split_len = pl.split_len;
+  p.n_splits = pl.n_splits;
+  p.total_groups = (int)groups;
+  const float scale = desc->scale > 0.f ? desc->scale : 1.0f / sqrtf((float)desc->D);
+  p.c = scale * 1.4426950408889634f;
+  hipError_t e = va::launch_scores(p, desc->D, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(VA_EHIP, "score kernel launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
 const char* va_status_str(va_status s) {
   switch (s) {
     case VA_OK: return "ok";

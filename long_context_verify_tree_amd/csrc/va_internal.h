@@ -74,7 +74,24 @@ struct CommitParams {
   int B, Hkv, N, capacity, es, row_bytes;
 };
 
-// Launchers (va_attn.hip, va_commit.hip).  Return the hipError_t of the launch.
+struct ScoreParams {
+  const void* q;        // [B, Hs, M, D] bf16 (strides qs)
+  const void* k;        // [B, Hs, L, D] bf16 (strides ks)
+  int64_t qs[3], ks[3];
+  float* score;         // [B, L] fp32, row stride ld_out
+  int64_t ld_out;
+  float* s;             // workspace: scaled scores [B, Hs, M, ld_s], log2 domain
+  float* stat_m;        // workspace: [B, Hs, M, n_splits] split max
+  float* stat_l;        // workspace: [B, Hs, M, n_splits] split sum
+  int64_t ld_s;         // L rounded up to 32
+  int B, Hs, M, L;
+  int split_len, n_splits, total_groups;
+  float c;              // scale * log2(e)
+};
+
+// Launchers (va_attn.hip, va_commit.hip, va_score.hip).  Return the
+// hipError_t of the launch.
+hipError_t launch_scores(const ScoreParams& p, int D, hipStream_t stream);
 hipError_t launch_commit(const CommitParams& p, hipStream_t stream);
 hipError_t launch_partials(const PartialParams& p, int dtype, int D, int rb, bool gather,
                            hipStream_t stream);

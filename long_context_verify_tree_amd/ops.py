@@ -59,6 +59,8 @@ def _declare(lib):
         "va_select_workspace_size": (i32, [i32, i32, ctypes.POINTER(sz)]),
         "select_verify_set": (i32, [_P, _P, i32, i32, i64, i32, i32, i32, i32, _P, _P, sz, _P]),
         "accept_commit": (i32, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
+        "va_scores_workspace_size": (i32, [_P, _P]),
+        "importance_scores": (i32, [_P, _P, _P, _P, i64, _P, sz, _P]),
         "va_status_str": (ctypes.c_char_p, [i32]),
         "va_last_error": (ctypes.c_char_p, []),
         "va_version": (i32, []),
@@ -249,6 +251,51 @@ def select_verify_set(draft_score, target_score, *, sink: int, window: int, top_
                                   sink, window, top_m, budget, _ptr(out), _ptr(workspace),
                                   workspace.numel() if workspace is not None else 0,
                                   _stream(draft_score.device)))
+    return out
+
+
+class ScoreDesc(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("Hs", ctypes.c_int32), ("M", ctypes.c_int32), ("D", ctypes.c_int32),
+                ("L", ctypes.c_int32), ("dtype", ctypes.c_int32), ("scale", ctypes.c_float),
+                ("q_stride", ctypes.c_int64 * 3), ("k_stride", ctypes.c_int64 * 3)]
+
+
+def make_score_desc(q, k, scale: Optional[float] = None) -> ScoreDesc:
+    """q [B, Hs, M, D], k [B, Hs, L, D] (bf16, unit innermost stride)."""
+    if q.dtype != torch.bfloat16 or k.dtype != torch.bfloat16:
+        raise ValueError("importance scores take bf16 q and k")
+    B, Hs, M, D = q.shape
+    if k.shape[:2] != (B, Hs) or k.shape[3] != D:
+        raise ValueError("k must be [B, Hs, L, D]")
+    d = ScoreDesc()
+    d.B, d.Hs, d.M, d.D, d.L, d.dtype = B, Hs, M, D, k.shape[2], VA_BF16
+    d.scale = 0.0 if scale is None else float(scale)
+    d.q_stride = _strides3(q)
+    d.k_stride = _strides3(k)
+    return d
+
+
+def scores_workspace_size(desc: ScoreDesc) -> int:
+    load()
+    n = ctypes.c_size_t()
+    _check(_lib.va_scores_workspace_size(ctypes.byref(desc), ctypes.byref(n)))
+    return n.value
+
+
+def importance_scores(q, k, scale: Optional[float] = None, out=None, workspace=None,
+                      desc: Optional[ScoreDesc] = None) -> torch.Tensor:
+    """Global importance map [B, L] float32 from the scoring heads' q and k."""
+    load()
+    if desc is None:
+        desc = make_score_desc(q, k, scale)
+    if out is None:
+        out = torch.empty(desc.B, desc.L, dtype=torch.float32, device=q.device)
+    if out.dtype != torch.float32 or out.stride(1) != 1:
+        raise ValueError("out must be float32 with contiguous rows")
+    if workspace is None:
+        workspace = torch.empty(scores_workspace_size(desc), dtype=torch.uint8, device=q.device)
+    _check(_lib.importance_scores(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(out), out.stride(0), _ptr(workspace),
+                                  workspace.numel(), _stream(q.device)))
     return out
 
 
