@@ -28,6 +28,12 @@ the pages by eye:
   spell the aggregation out; the plain reading taken here is the sum, over
   the scoring heads and their query rows, of the attention probabilities
   each row gives to every context token.
+* ``best_first_tree`` builds the draft tree the verification takes
+  (BASTION, "Drafting a Diffusione a Blocchi Basato su Albero" and
+  "Surrogato di Accettazione ed Espansione Best-First"): from per-position
+  candidate tokens with their marginal probabilities it adds, N times, the
+  valid node (a child of the tree or of the root) with the highest path score
+  rho = product of the marginals along the path.
 * ``select_verify_set`` follows the selection rule of Dustin, "Metodologia"
   section 1 (Aggregazione Ibrida dell'Attenzione): protect an attention-sink
   prefix and a local window of recent tokens, then fill the remaining budget
@@ -48,7 +54,12 @@ design notes of the repository):
   -0 equals +0; the output index list is ascending;
 * ``lse`` is the natural-log log-sum-exp of the scaled scores of a row;
 * importance scores: the softmax of a scoring row runs over the context
-  tokens [0, L) only, and the map is the plain sum of the probabilities.
+  tokens [0, L) only, and the map is the plain sum of the probabilities;
+* draft tree: position k's candidates are ranked by probability (ties: lower
+  candidate index); rho is accumulated in float32, parent first; equal rho
+  goes to the node whose parent entered the tree first, then to the better
+  ranked candidate; probabilities that are NaN or negative count as 0; the
+  expected acceptance surrogate is the float32 sum of rho in node order.
 
 Parity status: every function here is pinned by the ``-m "not gpu"`` tests
 (closed forms, textbook special cases, brute force); none is "parity
@@ -324,3 +335,55 @@ def importance_scores(q: np.ndarray, k: np.ndarray, scale: Optional[float] = Non
             p = np.exp(s)
             out[b] += (p / p.sum(axis=1, keepdims=True)).sum(axis=0)
     return out
+
+
+# ---------------------------------------------------------------------------
+# best-first draft tree
+
+
+def best_first_tree(cand_prob: np.ndarray, cand_token: np.ndarray, N: int):
+    """Best-first prefix tree of N draft nodes for one sequence (BASTION,
+    "Surrogato di Accettazione ed Espansione Best-First").
+
+    cand_prob, cand_token [K, T]: the T candidate tokens of each of the K
+    block positions and their marginal probabilities q_k.  A node at depth d
+    is a choice of one candidate at each of positions 0..d-1; its path score
+    is rho = q_0 * ... * q_{d-1} (float32, in that order).  Starting from an
+    empty tree whose only valid node is the best candidate of position 0,
+    each step adds the valid node of highest rho; adding a node makes valid
+    its best child (next position) and its next sibling (same parent, next
+    candidate of the same position).  Returns parent [N] (-1: child of the
+    committed context), token [N], rho [N] (float32) and the surrogate
+    A_hat = sum of rho (float32, node order).
+    """
+    cand_prob = np.asarray(cand_prob, dtype=np.float32)
+    K, T = cand_prob.shape
+    prob = np.where(cand_prob > 0, cand_prob, np.float32(0))     # NaN and negatives count as 0
+    order = [np.lexsort((np.arange(T), -prob[k].astype(np.float64))) for k in range(K)]
+    q = np.stack([prob[k][order[k]] for k in range(K)])          # [K, T], descending per position
+    tok = np.stack([np.asarray(cand_token)[k][order[k]] for k in range(K)])
+    if sum(T ** d for d in range(1, K + 1)) < N:
+        raise ValueError("fewer prefixes than N")
+    import heapq
+    one = np.float32(1.0)
+    # heap entries: (-rho, parent node (-1 first), rank, depth, rho of the parent)
+    heap = [(-float(q[0, 0]), -1, 0, 1, one)]
+    parent, token, rho = [], [], []
+    while len(parent) < N:
+        neg, par, rank, depth, rho_par = heapq.heappop(heap)
+        node = len(parent)
+        r = np.float32(rho_par * q[depth - 1, rank])
+        parent.append(par)
+        token.append(int(tok[depth - 1, rank]))
+        rho.append(r)
+        if depth < K:                                    # best child
+            c = np.float32(r * q[depth, 0])
+            heapq.heappush(heap, (-float(c), node, 0, depth + 1, r))
+        if rank + 1 < T:                                 # next sibling
+            sib = np.float32(rho_par * q[depth - 1, rank + 1])
+            heapq.heappush(heap, (-float(sib), par, rank + 1, depth, rho_par))
+    a_hat = np.float32(0)
+    for r in rho:
+        a_hat = np.float32(a_hat + r)
+    return (np.array(parent, dtype=np.int32), np.array(token, dtype=np.int32),
+            np.array(rho, dtype=np.float32), a_hat)

@@ -636,3 +636,70 @@ def test_scores_bf16_bits_and_default_scale():
                                                     vo.bf16_bits_to_f64(kb).astype(np.float32)), rtol=1e-12)
     np.testing.assert_allclose(vo.importance_scores(q32, k32), vo.importance_scores(q32, k32, scale=1 / 8.0),
                                rtol=1e-14)
+
+
+# ---------------------------------------------------------------------------
+# best-first draft tree (BASTION, "Surrogato di Accettazione ed Espansione
+# Best-First": best-first expansion maximises the summed path scores)
+
+
+def _paths(parent, token):
+    out = []
+    for i in range(len(parent)):
+        p, j = [], i
+        while j != -1:
+            p.append(int(token[j]))
+            j = int(parent[j])
+        out.append(tuple(p[::-1]))
+    return out
+
+
+@pytest.mark.parametrize("seed,K,T,N", [(0, 3, 3, 10), (1, 4, 2, 20), (2, 2, 5, 30), (3, 5, 3, 40)])
+def test_tree_is_the_top_n_prefixes_by_brute_force(seed, K, T, N):
+    # rho never grows along a path (every q <= 1), so the best-first tree is
+    # exactly the N prefixes of largest rho; enumerate all of them
+    rng = np.random.default_rng(seed)
+    prob = rng.random((K, T)).astype(np.float32)
+    tok = (100 * np.arange(K)[:, None] + np.arange(T)[None, :]).astype(np.int32)
+    parent, token, rho, a_hat = vo.best_first_tree(prob, tok, N)
+    scores = {}
+    for d in range(1, K + 1):
+        for choice in itertools.product(range(T), repeat=d):
+            r = np.float32(1)
+            for k, j in enumerate(choice):
+                r = np.float32(r * prob[k, j])
+            scores[tuple(int(tok[k, j]) for k, j in enumerate(choice))] = r
+    best = sorted(scores, key=lambda s: -scores[s])[:N]
+    got = _paths(parent, token)
+    assert set(got) == set(best)
+    assert all(parent[i] < i for i in range(N))                       # topological, prefix-closed
+    np.testing.assert_array_equal(rho, np.array([scores[g] for g in got], dtype=np.float32))
+    assert (np.diff(rho.astype(np.float64)) <= 0).all()                # diminishing returns
+    np.testing.assert_allclose(a_hat, rho.astype(np.float64).sum(), rtol=1e-6)
+
+
+def test_tree_equal_probabilities_hand_order():
+    # K=2, T=2, every q = 1/2: the root's two candidates (rho 1/2) come
+    # first, then the children of node 0 (parent 0 before parent 1), then
+    # those of node 1: parents [-1, -1, 0, 0, 1, 1]
+    prob = np.full((2, 2), 0.5, dtype=np.float32)
+    tok = np.array([[7, 8], [9, 10]], dtype=np.int32)
+    parent, token, rho, a_hat = vo.best_first_tree(prob, tok, 6)
+    assert list(parent) == [-1, -1, 0, 0, 1, 1]
+    assert list(token) == [7, 8, 9, 10, 9, 10]
+    assert list(rho) == [0.5, 0.5, 0.25, 0.25, 0.25, 0.25]
+    assert a_hat == np.float32(2.0)
+
+
+def test_tree_single_candidate_is_a_chain_and_specials():
+    prob = np.array([[0.9], [0.5], [0.7]], dtype=np.float32)
+    parent, token, rho, _ = vo.best_first_tree(prob, np.array([[1], [2], [3]]), 3)
+    assert list(parent) == [-1, 0, 1] and list(token) == [1, 2, 3]
+    assert list(rho) == [np.float32(0.9), np.float32(np.float32(0.9) * np.float32(0.5)),
+                         np.float32(np.float32(np.float32(0.9) * np.float32(0.5)) * np.float32(0.7))]
+    # NaN / negative probabilities count as 0 and rank last; too few prefixes raise
+    prob2 = np.array([[np.nan, 0.2, -1.0]], dtype=np.float32)
+    parent2, token2, rho2, _ = vo.best_first_tree(prob2, np.array([[4, 5, 6]]), 3)
+    assert list(token2) == [5, 4, 6] and list(rho2) == [np.float32(0.2), 0.0, 0.0]
+    with pytest.raises(ValueError):
+        vo.best_first_tree(prob, np.array([[1], [2], [3]]), 4)
