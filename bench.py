@@ -189,13 +189,14 @@ SCORE_HEADS = 2   # scoring heads of the importance map (a few selected heads)
 
 
 def measure_scores(torch, ops, cfg, base, dev, step_ms, reps: int = 20):
-    """Importance map of SCORE_HEADS scoring heads with the N draft rows
-    each, over the benchmarked cache's first KV heads; mean of `reps` calls
-    timed with HIP events on the launching stream."""
+    """Importance map of SCORE_HEADS scoring heads with (up to 32 of) the
+    draft rows each, over the benchmarked cache's first KV heads; mean of
+    `reps` calls timed with HIP events on the launching stream."""
     if cfg.dtype != "bf16" or cfg.L == 0:
         return None
     hs = min(SCORE_HEADS, cfg.Hkv)
-    q = base["q"][:, :hs]
+    rows = min(cfg.N, 32)                      # scoring rows per head (the kernel takes up to 32)
+    q = base["q"][:, :hs, :rows]
     k = base["k_cache"][:, :hs]
     desc = ops.make_score_desc(q, k)
     ws = torch.empty(ops.scores_workspace_size(desc), dtype=torch.uint8, device=dev)
@@ -209,12 +210,35 @@ def measure_scores(torch, ops, cfg, base, dev, step_ms, reps: int = 20):
     b.record()
     b.synchronize()
     us = a.elapsed_time(b) * 1e3 / reps
-    nbytes = cfg.B * hs * (cfg.L + cfg.N) * cfg.D * 2 + cfg.B * cfg.L * 4   # K and q read, map written
+    nbytes = cfg.B * hs * (cfg.L + rows) * cfg.D * 2 + cfg.B * cfg.L * 4   # K and q read, map written
     return {"us": round(us, 2), "bytes": nbytes, "gbs": round(nbytes / (us * 1e-6) / 1e9, 1),
             "frac_of_hbm_peak": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
-            "scoring_heads": hs, "rows_per_head": cfg.N,
+            "scoring_heads": hs, "rows_per_head": rows,
             "vs_one_verification_step": round(us * 1e-3 / step_ms, 4),
             "kernels": ["score_partial_kernel", "score_finish_kernel"]}
+
+
+TREE_POSITIONS, TREE_CANDIDATES = 16, 8   # block positions and candidates per position of the drafter
+
+
+def measure_tree(torch, ops, cfg, dev, reps: int = 20):
+    """Best-first draft tree of the workload's N nodes per sequence from
+    seeded synthetic candidates (Dirichlet(0.3) marginals over
+    TREE_CANDIDATES tokens at each of TREE_POSITIONS positions)."""
+    rng = np.random.default_rng(cfg.seed + 9)
+    K, T = TREE_POSITIONS, TREE_CANDIDATES
+    prob = torch.from_numpy(rng.dirichlet(np.full(T, 0.3), size=(cfg.B, K)).astype(np.float32)).to(dev)
+    tok = torch.from_numpy(rng.integers(0, 1 << 17, (cfg.B, K, T)).astype(np.int32)).to(dev)
+    res = ops.build_draft_tree(prob, tok, cfg.N)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        ops.build_draft_tree(prob, tok, cfg.N)
+    b.record()
+    b.synchronize()
+    return {"us": round(a.elapsed_time(b) * 1e3 / reps, 2), "nodes": cfg.N, "positions": K, "candidates": T,
+            "mean_a_hat": round(float(res[3].mean().item()), 4), "kernel": "tree_kernel"}
 
 
 def main():
@@ -379,6 +403,7 @@ def main():
     roof["traffic"], roof["traffic_source"] = committed_traffic(kernel, cfg.name)
     line["accept_commit"] = measure_commit(torch, ops, cfg, x, base, dev)
     line["importance_scores"] = measure_scores(torch, ops, cfg, base, dev, ms_per_step)
+    line["draft_tree"] = measure_tree(torch, ops, cfg, dev)
     if args.copy_calib_gib > 0:
         n = int(args.copy_calib_gib * (1 << 30))
         src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)

@@ -156,6 +156,30 @@ va_status verify_attn_merge(const va_attn_desc* desc, int32_t n_ctx,
                             void* out, float* lse,
                             const void* ws, size_t ws_bytes, void* stream);
 
+/* Best-first draft tree (BASTION, "Drafting a Diffusione a Blocchi Basato su
+ * Albero" and "Surrogato di Accettazione ed Espansione Best-First").  A block
+ * drafter proposes, for each of K positions, T candidate tokens with their
+ * marginal probabilities.  A node at depth d picks one candidate at each of
+ * the first d positions; its path score is rho = q_0 * ... * q_{d-1}
+ * (float32, in that order).  The tree is grown by adding, N times, the valid
+ * node of highest rho (the root's best candidate first; adding a node makes
+ * its best child and its next sibling valid); ties go to the node whose
+ * parent entered first, then to the better-ranked candidate.  Candidates of
+ * a position are ranked by probability, ties to the lower candidate index;
+ * NaN or negative probabilities count as 0.
+ *   cand_prob   [B, K, T] float32 device, contiguous
+ *   cand_token  [B, K, T] int32 device, contiguous (token ids, copied out)
+ *   parent      [B, N] int32 device, written: node index (< own index) or -1
+ *   token       [B, N] int32 device, written: the node's token
+ *   rho         [B, N] float32 device, written: non-increasing per sequence
+ *   a_hat       [B] float32 device, written: sum of rho in node order (the
+ *               surrogate of the expected accepted length)
+ * 1 <= N <= 256, K x T <= 4096, and T + T^2 + ... + T^K >= N (else
+ * VA_EINVAL / VA_EUNSUPPORTED).  The parent array feeds verify_attn_*. */
+va_status build_draft_tree(const float* cand_prob, const int32_t* cand_token, int32_t B,
+                           int32_t K, int32_t T, int32_t N, int32_t* parent, int32_t* token,
+                           float* rho, float* a_hat, void* stream);
+
 /* Importance scores for the selector (Dustin, "Metodologia" sections 1-2:
  * attention scores of a few scoring heads -- the draft's lookahead rows or
  * the target's previous rows -- aggregated into one global importance map):

@@ -414,6 +414,29 @@ va_status importance_scores(const va_score_desc* desc, const void* q, const void
   return ok();
 }
 
+va_status build_draft_tree(const float* cand_prob, const int32_t* cand_token, int32_t B, int32_t K, int32_t T,
+                           int32_t N, int32_t* parent, int32_t* token, float* rho, float* a_hat, void* stream) {
+  if (B < 0) return fail(VA_EINVAL, "B must be >= 0");
+  if (K < 1 || T < 1 || N < 1) return fail(VA_EINVAL, "K, T and N must be >= 1");
+  if (N > va::kTreeMaxN) return fail(VA_EUNSUPPORTED, "N = %d exceeds %d nodes", N, va::kTreeMaxN);
+  if (T > 0xFFFF || (int64_t)K * T > va::kTreeMaxKT)
+    return fail(VA_EUNSUPPORTED, "K x T = %lld candidates exceed %d", (long long)K * T, va::kTreeMaxKT);
+  // prefixes available: T + T^2 + ... + T^K (saturating)
+  int64_t prefixes = 0, level = 1;
+  for (int d = 1; d <= K && prefixes < N; ++d) {
+    level = level * T > (int64_t)1 << 40 ? (int64_t)1 << 40 : level * T;
+    prefixes += level;
+  }
+  if (prefixes < N) return fail(VA_EINVAL, "only %lld prefixes for N = %d nodes", (long long)prefixes, N);
+  if (B == 0) return ok();
+  if (!cand_prob || !cand_token || !parent || !token || !rho || !a_hat)
+    return fail(VA_EINVAL, "every tensor of build_draft_tree must be non-NULL");
+  va::TreeParams p{cand_prob, cand_token, parent, token, rho, a_hat, B, K, T, N};
+  hipError_t e = va::launch_tree(p, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(VA_EHIP, "tree kernel launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
 const char* va_status_str(va_status s) {
   switch (s) {
     case VA_OK: return "ok";

@@ -89,8 +89,22 @@ struct ScoreParams {
   float c;              // scale * log2(e)
 };
 
-// Launchers (va_attn.hip, va_commit.hip, va_score.hip).  Return the
-// hipError_t of the launch.
+constexpr int kTreeMaxKT = 4096;   // K * T candidates per sequence
+constexpr int kTreeMaxN = 256;
+
+struct TreeParams {
+  const float* prob;      // [B, K, T]
+  const int32_t* tok;     // [B, K, T]
+  int32_t* parent;        // [B, N]
+  int32_t* token;         // [B, N]
+  float* rho;             // [B, N]
+  float* a_hat;           // [B]
+  int B, K, T, N;
+};
+
+// Launchers (va_attn.hip, va_commit.hip, va_score.hip, va_tree.hip).  Return
+// the hipError_t of the launch.
+hipError_t launch_tree(const TreeParams& p, hipStream_t stream);
 hipError_t launch_scores(const ScoreParams& p, int D, hipStream_t stream);
 hipError_t launch_commit(const CommitParams& p, hipStream_t stream);
 hipError_t launch_partials(const PartialParams& p, int dtype, int D, int rb, bool gather,

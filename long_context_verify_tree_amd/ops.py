@@ -60,6 +60,7 @@ def _declare(lib):
         "select_verify_set": (i32, [_P, _P, i32, i32, i64, i32, i32, i32, i32, _P, _P, sz, _P]),
         "accept_commit": (i32, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
         "va_scores_workspace_size": (i32, [_P, _P]),
+        "build_draft_tree": (i32, [_P, _P, i32, i32, i32, i32, _P, _P, _P, _P, _P]),
         "importance_scores": (i32, [_P, _P, _P, _P, i64, _P, sz, _P]),
         "va_status_str": (ctypes.c_char_p, [i32]),
         "va_last_error": (ctypes.c_char_p, []),
@@ -342,3 +343,26 @@ def accept_commit(k_cache, v_cache, k_draft, v_draft, parent, accepted, cache_le
     _check(_lib.accept_commit(ctypes.byref(desc), _ptr(k_cache), _ptr(v_cache), _ptr(k_draft), _ptr(v_draft),
                               _ptr(parent), _ptr(accepted), _ptr(cache_len), _ptr(new_len), _stream(k_cache.device)))
     return new_len
+
+
+def build_draft_tree(cand_prob, cand_token, N: int):
+    """Best-first draft tree of N nodes per sequence from candidates
+    cand_prob float32 [B, K, T] and cand_token int32 [B, K, T].
+    Returns (parent int32 [B, N], token int32 [B, N], rho float32 [B, N],
+    a_hat float32 [B])."""
+    load()
+    if cand_prob.dtype != torch.float32 or cand_token.dtype != torch.int32:
+        raise ValueError("cand_prob must be float32 and cand_token int32")
+    if cand_prob.dim() != 3 or cand_token.shape != cand_prob.shape:
+        raise ValueError("cand_prob and cand_token must both be [B, K, T]")
+    if not (cand_prob.is_contiguous() and cand_token.is_contiguous()):
+        raise ValueError("candidates must be contiguous")
+    B, K, T = cand_prob.shape
+    dev = cand_prob.device
+    parent = torch.empty(B, N, dtype=torch.int32, device=dev)
+    token = torch.empty(B, N, dtype=torch.int32, device=dev)
+    rho = torch.empty(B, N, dtype=torch.float32, device=dev)
+    a_hat = torch.empty(B, dtype=torch.float32, device=dev)
+    _check(_lib.build_draft_tree(_ptr(cand_prob), _ptr(cand_token), B, K, T, N, _ptr(parent), _ptr(token), _ptr(rho),
+                                 _ptr(a_hat), _stream(dev)))
+    return parent, token, rho, a_hat

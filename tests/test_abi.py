@@ -189,3 +189,14 @@ def test_commit_rejects_before_launch(ops):
     assert f(ctypes.byref(d), *a, None) == ops.VA_EINVAL
     d.D = 96
     assert f(ctypes.byref(d), *args, None) == ops.VA_EUNSUPPORTED
+
+
+def test_tree_rejects_before_launch(ops):
+    f = ops._lib.build_draft_tree
+    ok_args = (FAKE, FAKE, 2, 4, 3, 10, FAKE, FAKE, FAKE, FAKE, None)
+    assert f(*ok_args[:2], 2, 4, 3, 0, *ok_args[6:]) == ops.VA_EINVAL          # N < 1
+    assert f(*ok_args[:2], 2, 4, 3, 257, *ok_args[6:]) == ops.VA_EUNSUPPORTED  # N > 256
+    assert f(*ok_args[:2], 2, 64, 128, 10, *ok_args[6:]) == ops.VA_EUNSUPPORTED  # K x T > 4096
+    assert f(*ok_args[:2], 2, 2, 2, 7, *ok_args[6:]) == ops.VA_EINVAL          # only 2 + 4 prefixes
+    assert f(None, *ok_args[1:]) == ops.VA_EINVAL
+    assert f(*ok_args[:6], None, *ok_args[7:]) == ops.VA_EINVAL
