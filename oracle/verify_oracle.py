@@ -34,6 +34,13 @@ the pages by eye:
   candidate tokens with their marginal probabilities it adds, N times, the
   valid node (a child of the tree or of the root) with the highest path score
   rho = product of the marginals along the path.
+* ``verify_time_model`` and ``choose_tree_size`` follow BASTION's online
+  budget controller ("Controllore Online del Budget Consapevole
+  dell'Hardware"): a roofline estimate of the verification latency,
+  T_verify(N) = max(bytes(N) / bandwidth, flops(N) / compute) + overhead,
+  with the three constants calibrated from measured runs, and a stopping
+  rule that grows the tree while the estimated speedup
+  S(N) = A_hat(N) * L_AR / C(N) still increases.
 * ``select_verify_set`` follows the selection rule of Dustin, "Metodologia"
   section 1 (Aggregazione Ibrida dell'Attenzione): protect an attention-sink
   prefix and a local window of recent tokens, then fill the remaining budget
@@ -59,7 +66,11 @@ design notes of the repository):
   candidate index); rho is accumulated in float32, parent first; equal rho
   goes to the node whose parent entered the tree first, then to the better
   ranked candidate; probabilities that are NaN or negative count as 0; the
-  expected acceptance surrogate is the float32 sum of rho in node order.
+  expected acceptance surrogate is the float32 sum of rho in node order;
+* budget controller: C(N) = T_draft + T_verify(N) (the drafter's cost does
+  not depend on the tree shape), L_AR is the latency of one autoregressive
+  step, and "starts to decrease" means the tree stops at the first N with
+  S(N + 1) <= S(N).
 
 Parity status: every function here is pinned by the ``-m "not gpu"`` tests
 (closed forms, textbook special cases, brute force); none is "parity
@@ -387,3 +398,41 @@ def best_first_tree(cand_prob: np.ndarray, cand_token: np.ndarray, N: int):
         a_hat = np.float32(a_hat + r)
     return (np.array(parent, dtype=np.int32), np.array(token, dtype=np.int32),
             np.array(rho, dtype=np.float32), a_hat)
+
+
+# ---------------------------------------------------------------------------
+# budget controller (BASTION, "Controllore Online del Budget Consapevole
+# dell'Hardware")
+
+
+def verify_bytes_flops(B: int, Hq: int, Hkv: int, D: int, n_ctx: int, N: int, elem_bytes: int):
+    """Bytes one verification must move and flops it must do: the K/V rows
+    of the context once, the queries, the draft K/V rows, the output and its
+    log-sum-exp; 4 flops per (query row, context key, dimension)."""
+    kv = 2 * B * Hkv * n_ctx * D * elem_bytes
+    q = B * Hq * N * D * elem_bytes
+    draft = 2 * B * Hkv * N * D * elem_bytes
+    out = B * Hq * N * D * elem_bytes + B * Hq * N * 4
+    return kv + q + draft + out, 4 * B * Hq * N * n_ctx * D
+
+
+def verify_time_model(B: int, Hq: int, Hkv: int, D: int, n_ctx: int, N: int, elem_bytes: int,
+                      bandwidth: float, compute: float, overhead: float) -> float:
+    """Roofline estimate of T_verify(N) in seconds with calibrated constants."""
+    nbytes, flops = verify_bytes_flops(B, Hq, Hkv, D, n_ctx, N, elem_bytes)
+    return max(nbytes / bandwidth, flops / compute) + overhead
+
+
+def choose_tree_size(a_hat_cum: Sequence[float], t_verify: Sequence[float], t_draft: float, l_ar: float):
+    """Tree size from the stopping rule: a_hat_cum[n - 1] is the surrogate
+    A_hat of the best-first tree of n nodes, t_verify[n - 1] the estimated
+    T_verify(n).  Returns (N, S) with S[n - 1] = A_hat(n) * L_AR / C(n),
+    C(n) = t_draft + t_verify(n), and N the first n whose successor does not
+    improve S (or the largest n)."""
+    a = np.asarray(a_hat_cum, dtype=np.float64)
+    t = np.asarray(t_verify, dtype=np.float64)
+    S = a * l_ar / (t_draft + t)
+    n = 1
+    while n < S.size and S[n] > S[n - 1]:
+        n += 1
+    return n, S

@@ -703,3 +703,45 @@ def test_tree_single_candidate_is_a_chain_and_specials():
     assert list(token2) == [5, 4, 6] and list(rho2) == [np.float32(0.2), 0.0, 0.0]
     with pytest.raises(ValueError):
         vo.best_first_tree(prob, np.array([[1], [2], [3]]), 4)
+
+
+# ---------------------------------------------------------------------------
+# budget controller (BASTION, "Controllore Online del Budget Consapevole
+# dell'Hardware")
+
+
+def test_time_model_regimes_and_ridge():
+    # headline shape: memory-bound at N = 1, compute-bound at N = 256; the
+    # switch happens where flops / bytes crosses compute / bandwidth
+    args = dict(B=8, Hq=32, Hkv=8, D=128, n_ctx=32768, elem_bytes=2)
+    bw, fl, c0 = 5.5e12, 1.0e15, 5e-6
+    nb1, f1 = vo.verify_bytes_flops(N=1, **args)
+    assert vo.verify_time_model(N=1, bandwidth=bw, compute=fl, overhead=c0, **args) == pytest.approx(nb1 / bw + c0)
+    nb2, f2 = vo.verify_bytes_flops(N=256, **args)
+    assert vo.verify_time_model(N=256, bandwidth=bw, compute=fl, overhead=c0, **args) == pytest.approx(f2 / fl + c0)
+    # bytes: 2 B Hkv L D e of K/V plus the N-dependent rows
+    assert nb1 == 2 * 8 * 8 * 32768 * 128 * 2 + 8 * 32 * 128 * 2 + 2 * 8 * 8 * 128 * 2 + 8 * 32 * 128 * 2 + 8 * 32 * 4
+    assert f1 == 4 * 8 * 32 * 32768 * 128
+    ts = [vo.verify_time_model(N=n, bandwidth=bw, compute=fl, overhead=c0, **args) for n in range(1, 257)]
+    assert all(b >= a for a, b in zip(ts, ts[1:]))                     # never faster with more nodes
+    # the regime changes where flops / bytes passes the ridge compute / bandwidth:
+    # flops / bytes ~ 4 Hq N L D / (4 Hkv L D) = (Hq / Hkv) N, so N ~ ridge * Hkv / Hq = 45.5
+    knee = next(n for n in range(1, 257)
+                if vo.verify_bytes_flops(N=n, **args)[1] / fl > vo.verify_bytes_flops(N=n, **args)[0] / bw)
+    assert knee == math.ceil(fl / bw * 8 / 32)
+
+
+def test_controller_stops_at_the_first_decrease():
+    # A_hat(n) = n (every node accepted) and a flat cost: S grows to the end
+    n, S = vo.choose_tree_size(np.arange(1, 11), np.full(10, 1.0), t_draft=0.0, l_ar=1.0)
+    assert n == 10
+    # A_hat(n) = 1 - 2^-n, cost 1 + 0.1 n: S(n) = (1 - 2^-n) / (1 + 0.1 n)
+    a = 1 - 0.5 ** np.arange(1, 21)
+    t = 1 + 0.1 * np.arange(1, 21)
+    n, S = vo.choose_tree_size(a, t, t_draft=0.0, l_ar=1.0)
+    brute = [(1 - 0.5 ** k) / (1 + 0.1 * k) for k in range(1, 21)]
+    np.testing.assert_allclose(S, brute, rtol=1e-12)
+    assert n == int(np.argmax(brute)) + 1 == 3
+    # a later, higher bump is not reached: the rule stops at the first decrease
+    n, _ = vo.choose_tree_size([1.0, 2.0, 1.5, 9.0], [1.0, 1.0, 1.0, 1.0], t_draft=0.0, l_ar=1.0)
+    assert n == 2
