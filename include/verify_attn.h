@@ -180,6 +180,30 @@ va_status build_draft_tree(const float* cand_prob, const int32_t* cand_token, in
                            int32_t K, int32_t T, int32_t N, int32_t* parent, int32_t* token,
                            float* rho, float* a_hat, void* stream);
 
+/* Tree-budget controller (BASTION, "Controllore Online del Budget
+ * Consapevole dell'Hardware"): a roofline estimate of the verification
+ * latency and the rule that sizes the draft tree.  Host functions; no GPU
+ * work.
+ *
+ * va_verify_time_model: T_verify(N) = max(bytes(N) / bandwidth,
+ * flops(N) / compute) + overhead in seconds for desc's shape with N draft
+ * nodes over n_ctx context keys; bytes(N) = 2 B Hkv n_ctx D e (context K/V)
+ * + B Hq N D e (queries) + 2 B Hkv N D e (draft K/V) + B Hq N (D e + 4)
+ * (output and lse), flops(N) = 4 B Hq N n_ctx D, e = element bytes.  The
+ * three constants are calibrated from measured runs (desc->N is ignored). */
+va_status va_verify_time_model(const va_attn_desc* desc, int32_t n_ctx, double bandwidth,
+                               double compute, double overhead, int32_t N, double* seconds);
+
+/* va_choose_tree_size: the tree stops growing when the estimated speedup
+ * S(n) = a_hat_cum[n-1] * l_ar / (t_draft + t_verify[n-1]) stops increasing:
+ * *n_best = the first n with S(n+1) <= S(n), or n_max.  a_hat_cum[n-1] is the
+ * surrogate of the best-first tree of n nodes (prefix sums of
+ * build_draft_tree's rho), t_verify[n-1] the (estimated) verification time
+ * of n nodes, t_draft the drafter's time, l_ar one autoregressive step's
+ * time (seconds).  Host pointers. */
+va_status va_choose_tree_size(const float* a_hat_cum, const double* t_verify, int32_t n_max,
+                              double t_draft, double l_ar, int32_t* n_best);
+
 /* Importance scores for the selector (Dustin, "Metodologia" sections 1-2:
  * attention scores of a few scoring heads -- the draft's lookahead rows or
  * the target's previous rows -- aggregated into one global importance map):

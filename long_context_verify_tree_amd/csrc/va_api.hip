@@ -437,6 +437,36 @@ va_status build_draft_tree(const float* cand_prob, const int32_t* cand_token, in
   return ok();
 }
 
+va_status va_verify_time_model(const va_attn_desc* desc, int32_t n_ctx, double bandwidth, double compute,
+                               double overhead, int32_t N, double* seconds) {
+  va_status st = check_desc(desc);
+  if (st != VA_OK) return st;
+  if (!seconds) return fail(VA_EINVAL, "seconds is NULL");
+  if (n_ctx < 0 || N < 1) return fail(VA_EINVAL, "n_ctx >= 0 and N >= 1 required");
+  if (!(bandwidth > 0.0) || !(compute > 0.0) || !(overhead >= 0.0))
+    return fail(VA_EINVAL, "bandwidth and compute must be > 0, overhead >= 0");
+  const double e = desc->dtype == VA_BF16 ? 2.0 : 4.0;
+  const double B = desc->B, Hq = desc->Hq, Hkv = desc->Hkv, D = desc->D, L = n_ctx, n = N;
+  const double bytes = 2.0 * B * Hkv * L * D * e + B * Hq * n * D * e + 2.0 * B * Hkv * n * D * e +
+                       B * Hq * n * D * e + B * Hq * n * 4.0;
+  const double flops = 4.0 * B * Hq * n * L * D;
+  const double tb = bytes / bandwidth, tf = flops / compute;
+  *seconds = (tb > tf ? tb : tf) + overhead;
+  return ok();
+}
+
+va_status va_choose_tree_size(const float* a_hat_cum, const double* t_verify, int32_t n_max, double t_draft,
+                              double l_ar, int32_t* n_best) {
+  if (!a_hat_cum || !t_verify || !n_best) return fail(VA_EINVAL, "a_hat_cum, t_verify and n_best must be non-NULL");
+  if (n_max < 1) return fail(VA_EINVAL, "n_max must be >= 1");
+  if (!(t_draft >= 0.0) || !(l_ar > 0.0)) return fail(VA_EINVAL, "t_draft >= 0 and l_ar > 0 required");
+  auto speedup = [&](int n) { return (double)a_hat_cum[n - 1] * l_ar / (t_draft + t_verify[n - 1]); };
+  int n = 1;
+  while (n < n_max && speedup(n + 1) > speedup(n)) ++n;
+  *n_best = n;
+  return ok();
+}
+
 const char* va_status_str(va_status s) {
   switch (s) {
     case VA_OK: return "ok";

@@ -17,6 +17,7 @@ import ctypes
 import os
 from typing import Optional, Tuple
 
+import numpy as np
 import torch  # noqa: F401  -- must be loaded first so the library binds to torch's HIP runtime
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -61,6 +62,8 @@ def _declare(lib):
         "accept_commit": (i32, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
         "va_scores_workspace_size": (i32, [_P, _P]),
         "build_draft_tree": (i32, [_P, _P, i32, i32, i32, i32, _P, _P, _P, _P, _P]),
+        "va_verify_time_model": (i32, [_P, i32, ctypes.c_double, ctypes.c_double, ctypes.c_double, i32, _P]),
+        "va_choose_tree_size": (i32, [_P, _P, i32, ctypes.c_double, ctypes.c_double, _P]),
         "importance_scores": (i32, [_P, _P, _P, _P, i64, _P, sz, _P]),
         "va_status_str": (ctypes.c_char_p, [i32]),
         "va_last_error": (ctypes.c_char_p, []),
@@ -366,3 +369,24 @@ def build_draft_tree(cand_prob, cand_token, N: int):
     _check(_lib.build_draft_tree(_ptr(cand_prob), _ptr(cand_token), B, K, T, N, _ptr(parent), _ptr(token), _ptr(rho),
                                  _ptr(a_hat), _stream(dev)))
     return parent, token, rho, a_hat
+
+
+def verify_time_model(desc: AttnDesc, n_ctx: int, bandwidth: float, compute: float, overhead: float, N: int) -> float:
+    """Roofline estimate of the verification time (seconds) of N draft nodes."""
+    load()
+    out = ctypes.c_double()
+    _check(_lib.va_verify_time_model(ctypes.byref(desc), n_ctx, bandwidth, compute, overhead, N, ctypes.byref(out)))
+    return out.value
+
+
+def choose_tree_size(a_hat_cum, t_verify, t_draft: float, l_ar: float) -> int:
+    """Tree size from the stop-at-first-decrease rule (host arrays)."""
+    load()
+    a = np.ascontiguousarray(np.asarray(a_hat_cum, dtype=np.float32))
+    t = np.ascontiguousarray(np.asarray(t_verify, dtype=np.float64))
+    if a.shape != t.shape or a.ndim != 1:
+        raise ValueError("a_hat_cum and t_verify must be 1-D of equal length")
+    n = ctypes.c_int32()
+    _check(_lib.va_choose_tree_size(a.ctypes.data_as(ctypes.c_void_p), t.ctypes.data_as(ctypes.c_void_p), a.size,
+                                    t_draft, l_ar, ctypes.byref(n)))
+    return n.value

@@ -6,6 +6,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -200,3 +201,26 @@ def test_tree_rejects_before_launch(ops):
     assert f(*ok_args[:2], 2, 2, 2, 7, *ok_args[6:]) == ops.VA_EINVAL          # only 2 + 4 prefixes
     assert f(None, *ok_args[1:]) == ops.VA_EINVAL
     assert f(*ok_args[:6], None, *ok_args[7:]) == ops.VA_EINVAL
+
+
+def test_controller_host_functions_match_the_oracle(ops):
+    # host functions of the library: no GPU involved
+    from oracle import verify_oracle as vo
+    d = good_desc(ops, B=8, Hq=32, Hkv=8, D=128, L=32768, N=8)
+    rng = np.random.default_rng(3)
+    for _ in range(20):
+        bw, fl, c0 = rng.uniform(1e12, 8e12), rng.uniform(1e14, 2.5e15), rng.uniform(0, 1e-5)
+        n_ctx, N = int(rng.integers(0, 1 << 17)), int(rng.integers(1, 257))
+        got = ops.verify_time_model(d, n_ctx, bw, fl, c0, N)
+        want = vo.verify_time_model(8, 32, 8, 128, n_ctx, N, 2, bw, fl, c0)
+        assert got == pytest.approx(want, rel=1e-12)
+    for _ in range(50):
+        n = int(rng.integers(1, 40))
+        a = np.cumsum(rng.random(n) ** 2).astype(np.float32)
+        t = np.sort(rng.uniform(1e-4, 3e-4, n))
+        t_draft, l_ar = float(rng.uniform(0, 1e-4)), float(rng.uniform(1e-4, 2e-4))
+        assert ops.choose_tree_size(a, t, t_draft, l_ar) == vo.choose_tree_size(a, t, t_draft, l_ar)[0]
+    with pytest.raises(ops.VerifyAttnError):
+        ops.verify_time_model(d, 100, 0.0, 1e15, 0.0, 4)
+    with pytest.raises(ops.VerifyAttnError):
+        ops.choose_tree_size(np.ones(3), np.ones(3), 0.0, 0.0)
