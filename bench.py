@@ -241,6 +241,99 @@ def measure_tree(torch, ops, cfg, dev, reps: int = 20):
             "mean_a_hat": round(float(res[3].mean().item()), 4), "kernel": "tree_kernel"}
 
 
+SWEEP_N = (1, 2, 4, 8, 16, 32, 64, 96, 128, 192, 256)
+
+
+def sweep_n(args):
+    """T_verify(N) on the workload's context (K/V cache, batch, heads) for
+    best-first trees of N nodes built from synthetic drafter candidates;
+    least-squares calibration of the roofline model's bandwidth, compute and
+    overhead; the controller's tree size on the trees' surrogate curve."""
+    import torch
+    from scipy.optimize import least_squares
+    from long_context_verify_tree_amd import ops, synth
+
+    ops.load()
+    cfg = synth.CONFIGS[args.config]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    g = torch.Generator(device=dev)
+    g.manual_seed(cfg.seed)
+    dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    B, Hq, Hkv, D, L = cfg.B, cfg.Hq, cfg.Hkv, cfg.D, cfg.L
+    e = 2 if cfg.dtype == "bf16" else 4
+    kc = torch.randn(B, Hkv, L, D, device=dev, generator=g).to(dt)
+    vc = torch.randn(B, Hkv, L, D, device=dev, generator=g).to(dt)
+    # best-first trees of up to 256 nodes from seeded drafter candidates
+    rng = np.random.default_rng(cfg.seed + 9)
+    K, T = TREE_POSITIONS, TREE_CANDIDATES
+    prob = torch.from_numpy(rng.dirichlet(np.full(T, 0.3), size=(B, K)).astype(np.float32)).to(dev)
+    tok = torch.from_numpy(rng.integers(0, 1 << 17, (B, K, T)).astype(np.int32)).to(dev)
+    read_peak = measured_read_peak(torch, dev)
+    times = []
+    for N in SWEEP_N:
+        parent, _, rho, _ = ops.build_draft_tree(prob, tok, N)
+        q = torch.randn(B, Hq, N, D, device=dev, generator=g).to(dt)
+        kd = torch.randn(B, Hkv, N, D, device=dev, generator=g).to(dt)
+        vd = torch.randn(B, Hkv, N, D, device=dev, generator=g).to(dt)
+        out = torch.empty_like(q)
+        lse = torch.empty(B, Hq, N, dtype=torch.float32, device=dev)
+        desc = ops.make_desc(q, kc, vc, kd, vd, out)
+        ws = torch.empty(ops.workspace_size(desc, L), dtype=torch.uint8, device=dev)
+
+        def step():
+            ops.verify_attn_partials(desc, q, kc, vc, kd, vd, parent, ws)
+            ops.verify_attn_merge(desc, L, out, lse, ws)
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            step()
+        torch.cuda.synchronize()
+        times.append((time.perf_counter() - t0) / args.steps)
+        print(f"[sweep] N={N}: {times[-1] * 1e3:.4f} ms", file=sys.stderr, flush=True)
+    if cfg.N <= SWEEP_N[-1]:
+        rho_all = ops.build_draft_tree(prob, tok, SWEEP_N[-1])[2].cpu().numpy().astype(np.float64)
+    a_curve = np.cumsum(rho_all.mean(axis=0))          # surrogate of the best-first tree of n nodes
+
+    def nbytes(n):
+        return 2 * B * Hkv * L * D * e + B * Hq * n * D * e + 2 * B * Hkv * n * D * e + B * Hq * n * (D * e + 4)
+
+    def model(p, n):
+        bw, fl, c0 = np.exp(p)
+        return np.maximum(nbytes(n) / bw, 4.0 * B * Hq * n * L * D / fl) + c0
+    ns = np.array(SWEEP_N, dtype=np.float64)
+    ts = np.array(times)
+    fit = least_squares(lambda p: np.log(model(p, ns)) - np.log(ts),
+                        x0=np.log([5e12, 1e15, 5e-6]), bounds=(np.log([1e11, 1e12, 1e-8]), np.log([2e13, 5e15, 1e-2])))
+    bw, fl, c0 = (float(v) for v in np.exp(fit.x))
+    desc1 = ops.make_desc(torch.empty(B, Hq, 1, D, dtype=dt, device=dev), kc, vc,
+                          torch.empty(B, Hkv, 1, D, dtype=dt, device=dev), torch.empty(B, Hkv, 1, D, dtype=dt, device=dev),
+                          torch.empty(B, Hq, 1, D, dtype=dt, device=dev))
+    n_all = np.arange(1, SWEEP_N[-1] + 1)
+    t_model = np.array([ops.verify_time_model(desc1, L, bw, fl, c0, int(n)) for n in n_all])
+    knee = int(next((n for n in n_all if 4.0 * B * Hq * n * L * D / fl > nbytes(n) / bw), 0))
+    t_ar = float(t_model[0])                           # one autoregressive step's verification
+    n_best = ops.choose_tree_size(a_curve, t_model, t_draft=t_ar, l_ar=t_ar)
+    S = a_curve * t_ar / (t_ar + t_model)
+    line = {
+        "metric": "T_verify(N) sweep + tree-size controller",
+        "workload": cfg.name, "n_ctx_keys": L, "steps": args.steps, "warmup": args.warmup,
+        "N": list(SWEEP_N), "t_verify_ms": [round(t * 1e3, 4) for t in times],
+        "fit": {"bandwidth_gbs": round(bw / 1e9, 1), "compute_tflops": round(fl / 1e12, 1),
+                "overhead_us": round(c0 * 1e6, 2),
+                "max_rel_residual": round(float(np.max(np.abs(model(fit.x, ns) / ts - 1))), 4)},
+        "ridge_knee_N": knee, "measured_read_peak_gbs": read_peak,
+        "controller": {"t_draft": "= T_verify(1)", "l_ar": "= T_verify(1)", "n_best": n_best,
+                       "a_hat_at_n_best": round(float(a_curve[n_best - 1]), 4),
+                       "speedup_estimate_at_n_best": round(float(S[n_best - 1]), 4),
+                       "tree": f"best-first from Dirichlet(0.3) marginals, {TREE_POSITIONS} positions x "
+                               f"{TREE_CANDIDATES} candidates"},
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -250,6 +343,9 @@ def main():
     ap.add_argument("--copies", type=int, default=0, help="input copies rotated over steps (0: auto)")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--sweep-n", action="store_true",
+                    help="instead of the step benchmark: time verification for N = 1..256 draft nodes on the "
+                         "workload's cache, calibrate the roofline time model and run the tree-size controller")
     ap.add_argument("--no-read-probe", action="store_true",
                     help="skip the read-only HBM probe (counter-collection runs)")
     ap.add_argument("--copy-calib-gib", type=float, default=0.0,
@@ -260,6 +356,9 @@ def main():
         print(f"bench.py runs on one GPU only (asked for {args.gpus}); the kernels use no collectives",
               file=sys.stderr)
         sys.exit(2)
+    if args.sweep_n:
+        sweep_n(args)
+        return
 
     import torch
     from long_context_verify_tree_amd import ops, synth

@@ -78,7 +78,10 @@ va::Plan make_plan(const va_attn_desc* d, int32_t n_ctx) {
   // kernel (256 rows per workgroup); other bf16 shapes: 32-row tiles (the
   // row tiles of one split share that XCD's L2 and run in the same round,
   // so K/V still come from HBM about once); fp32: 32 or 64 rows.
-  pl.rb = (d->dtype == VA_BF16 && R > 64) ? va::kRowsKernel : (d->dtype == VA_BF16 || R <= 32 ? 1 : 2);
+#ifndef VA_ROWS_MIN_R
+#define VA_ROWS_MIN_R 64
+#endif
+  pl.rb = (d->dtype == VA_BF16 && R > VA_ROWS_MIN_R) ? va::kRowsKernel : (d->dtype == VA_BF16 || R <= 32 ? 1 : 2);
   const int rows_per_tile = pl.rb == va::kRowsKernel ? 256 : 32 * pl.rb;
   pl.row_tiles = (R + rows_per_tile - 1) / rows_per_tile;
   const int64_t pairs = (int64_t)d->B * d->Hkv * pl.row_tiles;
