@@ -109,7 +109,9 @@ struct KernelShape {
 #endif
 };
 
-template <class T, int D, int RB, bool GATHER>
+// NT: every K/V row is read by this workgroup only (one row tile per KV
+// head), so the loads carry the non-temporal hint.
+template <class T, int D, int RB, bool GATHER, bool NT = false>
 __global__ __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(KernelShape<RB, sizeof(T), D, GATHER>::waves_per_eu)))
 void partial_kernel(PartialParams p) {
@@ -213,8 +215,8 @@ void partial_kernel(PartialParams p) {
       ko = (uint32_t)key * kts_b + col_b;   // past the region: reads zeros
       vo = (uint32_t)key * vts_b + col_b;
     }
-    kr = buf_load16(krs, ko);
-    vr = buf_load16(vrs, vo);
+    kr = buf_load16<NT>(krs, ko);
+    vr = buf_load16<NT>(vrs, vo);
   };
   auto load_tile = [&](int t, int ix, u32x4 (&kr)[NCH], u32x4 (&vr)[NCH]) __attribute__((always_inline)) {
 #pragma unroll
@@ -587,7 +589,7 @@ void partial_kernel(PartialParams p) {
 constexpr int kRowsWaves = 8;
 constexpr int kRowsThreads = 64 * kRowsWaves;
 
-template <int D, bool GATHER>
+template <int D, bool GATHER, bool NT = false>
 __global__ __launch_bounds__(kRowsThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void rows_kernel(PartialParams p) {
   using T = uint16_t;
@@ -712,7 +714,7 @@ void rows_kernel(PartialParams p) {
 #pragma unroll
     for (int j = 0; j < NCT; ++j) {
       const bool isv = 64 * wave_u + kRowsThreads * j >= KCH;
-      rx[j] = buf_load16(isv ? vrs : krs, (isv ? vo : ko) + (uint32_t)col_t * 16u);
+      rx[j] = buf_load16<NT>(isv ? vrs : krs, (isv ? vo : ko) + (uint32_t)col_t * 16u);
     }
   };
   __shared__ int kval[2][kTileKeys];   // key of the staged tile exists
@@ -953,21 +955,31 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeParams p) {
     p.lse[prow] = wsum > 0.f ? (muse + log2f(wsum)) * 0.69314718055994530942f : -INFINITY;
 }
 
-template <class T, int D, int RB, bool G>
+template <class T, int D, int RB, bool G, bool NT = false>
 hipError_t launch_p(const PartialParams& p, hipStream_t stream) {
-  hipLaunchKernelGGL((partial_kernel<T, D, RB, G>), dim3(p.total_groups), dim3(kThreads), 0, stream, p);
+  hipLaunchKernelGGL((partial_kernel<T, D, RB, G, NT>), dim3(p.total_groups), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 
+// The non-temporal hint goes on dense bf16 reads with one row tile per KV
+// head (each K/V row read once); with several row tiles the later tiles
+// find the rows in L2.
 template <class T, int D>
 hipError_t launch_p_rb(const PartialParams& p, int rb, bool gather, hipStream_t stream) {
-  if (rb == 1) return gather ? launch_p<T, D, 1, true>(p, stream) : launch_p<T, D, 1, false>(p, stream);
+  if (rb == 1) {
+    if (gather) return launch_p<T, D, 1, true>(p, stream);
+    if (sizeof(T) == 2 && p.row_tiles == 1) return launch_p<T, D, 1, false, true>(p, stream);
+    return launch_p<T, D, 1, false>(p, stream);
+  }
   return gather ? launch_p<T, D, 2, true>(p, stream) : launch_p<T, D, 2, false>(p, stream);
 }
 
 template <int D, bool G>
 hipError_t launch_rows(const PartialParams& p, hipStream_t stream) {
-  hipLaunchKernelGGL((rows_kernel<D, G>), dim3(p.total_groups), dim3(kRowsThreads), 0, stream, p);
+  if (!G && p.row_tiles == 1)
+    hipLaunchKernelGGL((rows_kernel<D, G, true>), dim3(p.total_groups), dim3(kRowsThreads), 0, stream, p);
+  else
+    hipLaunchKernelGGL((rows_kernel<D, G>), dim3(p.total_groups), dim3(kRowsThreads), 0, stream, p);
   return hipGetLastError();
 }
 

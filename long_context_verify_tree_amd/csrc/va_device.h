@@ -67,15 +67,14 @@ __device__ inline rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   void* ub = (void*)(((uint64_t)hi << 32) | lo);
   return __builtin_amdgcn_make_buffer_rsrc(ub, (short)0, (int)__builtin_amdgcn_readfirstlane(bytes), 0x00020000);
 }
-// K/V rows are read exactly once per call: the loads carry the non-temporal
-// hint (cache-policy bit `nt`), which keeps them from displacing the
-// workspace and query lines in L2 and raised the streaming rate of the
-// partial kernel by ~8% (193 -> 178 us on the Llama-3-8B 32k workload).
-#ifndef VA_KV_CACHE_POLICY
-#define VA_KV_CACHE_POLICY 2
-#endif
+// buf_load16<true> carries the non-temporal hint (cache-policy bit `nt`)
+// for K/V rows that are read exactly once per call: they then do not
+// displace the workspace and query lines in L2 (partial kernel on the
+// Llama-3-8B 32k workload: 193 -> 178 us).  Rows that another row tile reads
+// again take the default policy: there the second read is an L2 hit.
+template <bool NT = false>
 __device__ inline u32x4 buf_load16(rsrc_t r, uint32_t off) {
-  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, VA_KV_CACHE_POLICY));
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, NT ? 2 : 0));
 }
 __device__ inline int buf_load_i32(rsrc_t r, uint32_t off) {
   return (int)__builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);

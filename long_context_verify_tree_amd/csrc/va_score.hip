@@ -81,7 +81,7 @@ __global__ __launch_bounds__(kSThreads) void score_partial_kernel(ScoreParams p)
   auto load = [&](int t) __attribute__((always_inline)) {
 #pragma unroll
     for (int cc = 0; cc < NCH; ++cc)
-      kr[cc] = buf_load16(krs, (uint32_t)(kb + kSTile * t + kk0 + KPC * cc) * kts_b + col_b);   // past L: zeros
+      kr[cc] = buf_load16<true>(krs, (uint32_t)(kb + kSTile * t + kk0 + KPC * cc) * kts_b + col_b);   // past L: zeros
   };
   if (wave < ntiles) load(wave);
   for (int t = wave; t < ntiles; t += kSWavesS) {
