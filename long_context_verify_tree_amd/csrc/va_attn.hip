@@ -920,24 +920,27 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeParams p) {
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) ws += __shfl_xor(ws, off);
     wsum += ws;
-    int s = 0;
-    for (; s + 8 <= cnt; s += 8) {
-      float v[8][PER];
+    // groups of MG parts: all loads of a group are issued together (parts
+    // past the end re-read the last one and get weight 0), so a row costs
+    // one memory round trip per MG parts
+#ifndef VA_MERGE_GROUP
+#define VA_MERGE_GROUP 4
+#endif
+    constexpr int MG = VA_MERGE_GROUP;
+    for (int s = 0; s < cnt; s += MG) {
+      float v[MG][PER];
 #pragma unroll
-      for (int u = 0; u < 8; ++u)
+      for (int u = 0; u < MG; ++u) {
+        const int su = s + u < cnt ? s + u : cnt - 1;
 #pragma unroll
-        for (int e = 0; e < PER; ++e) v[u][e] = po[(int64_t)(s0 + s + u) * D + e];
+        for (int e = 0; e < PER; ++e) v[u][e] = po[(int64_t)(s0 + su) * D + e];
+      }
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const float w = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wl), s + u));
+      for (int u = 0; u < MG; ++u) {
+        const float w = s + u < cnt ? __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wl), s + u)) : 0.f;
 #pragma unroll
         for (int e = 0; e < PER; ++e) acc[e] = fmaf(w, v[u][e], acc[e]);
       }
-    }
-    for (; s < cnt; ++s) {
-      const float w = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wl), s));
-#pragma unroll
-      for (int e = 0; e < PER; ++e) acc[e] = fmaf(w, po[(int64_t)(s0 + s) * D + e], acc[e]);
     }
   }
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
