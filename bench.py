@@ -51,7 +51,8 @@ def algorithmic(cfg, n_ctx: int, sparse: bool):
 
 
 CSRC = os.path.join(ROOT, "long_context_verify_tree_amd", "csrc")
-KERNEL_SOURCES = {"partial_kernel": "va_attn.hip", "rows_kernel": "va_attn.hip", "select_kernel": "va_select.hip"}
+KERNEL_SOURCES = {"partial_kernel": "va_attn.hip", "rows_kernel": "va_attn.hip", "select_kernel": "va_select.hip",
+                  "score_partial_kernel": "va_score.hip"}
 
 
 def committed_traffic(kernel: str, workload: str):
