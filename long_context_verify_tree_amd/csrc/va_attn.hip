@@ -102,11 +102,7 @@ struct KernelShape {
   // one tile each in flight beat one wavefront with a two-tile ring.
   static constexpr bool lat_shape = hbm_shape && GATHER;
   static constexpr int prefetch = lat_shape ? 1 : (hbm_shape ? (D == 128 ? VA_RING_TILES : 2) : 1);
-#ifdef VA_HBM_WAVES_PER_EU
-  static constexpr int waves_per_eu = hbm_shape ? VA_HBM_WAVES_PER_EU : 1;
-#else
   static constexpr int waves_per_eu = hbm_shape && prefetch == 1 ? 2 : 1;
-#endif
 };
 
 // NT: every K/V row is read by this workgroup only (one row tile per KV
@@ -487,9 +483,6 @@ void partial_kernel(PartialParams p) {
         vmask[pp] = tile_mask(tn, ixr[pp]);
         ixr[pp] = load_idx(tile_of(k + pp + 2 * PF));
         compute(tile_of(k + pp), vm, masked_tag);
-#ifdef VA_SLOT_FENCE
-        __builtin_amdgcn_sched_barrier(0);
-#endif
       }
     }
     return k;
