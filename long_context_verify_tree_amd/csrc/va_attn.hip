@@ -317,7 +317,7 @@ void partial_kernel(PartialParams p) {
         }
         tmax = fmaxf(tmax, s[rb][e]);
       }
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+      tmax = half_max(tmax);
       const bool grow = (tmax - m_run[rb]) * c > 8.f;   // false when both are -inf (NaN)
       if (__any(grow)) {
         const float mnew = grow ? tmax : m_run[rb];
@@ -506,7 +506,7 @@ void partial_kernel(PartialParams p) {
   // ---- merge the four wavefronts (fixed order: 3 -> 2 -> 1 -> 0)
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
-    l_run[rb] += __shfl_xor(l_run[rb], 32);
+    l_run[rb] = half_sum(l_run[rb]);
     if (h == 0) mbuf[wave][rb][n] = m_run[rb];
   }
   __syncthreads();
@@ -573,12 +573,13 @@ void partial_kernel(PartialParams p) {
 
 // Many query rows per KV head (a large draft tree times the GQA group).
 // Eight wavefronts own 32 query rows each (256 rows per workgroup) and share
-// every 32-key K/V tile through a two-stage LDS buffer, so K/V bytes are
-// read once per 256 rows.  Two wavefronts per SIMD let one wavefront's
-// softmax overlap the other's MFMAs.  The workgroup's threads keep a ring of
-// RING tiles of 16-byte chunks in flight in registers; one LDS barrier per
-// tile.  Every wavefront sees every key of the part, so its rows' partials
-// are written directly.
+// every 32-key K/V tile through a three-stage LDS buffer, so K/V bytes are
+// read once per 256 rows.  Each wavefront issues the QK MFMAs of the next
+// tile before the softmax of the current one, and two wavefronts per SIMD
+// let one wavefront's softmax overlap the other's MFMAs.  The workgroup's
+// threads keep a ring of RING tiles of 16-byte chunks in flight in
+// registers; one LDS barrier per tile.  Every wavefront sees every key of
+// the part, so its rows' partials are written directly.
 constexpr int kRowsWaves = 8;
 constexpr int kRowsThreads = 64 * kRowsWaves;
 
@@ -589,15 +590,25 @@ void rows_kernel(PartialParams p) {
   constexpr int VEC = 8;
   constexpr int CPR = D / VEC;
   constexpr int GROWS = 32 * kRowsWaves;             // rows per workgroup
-  constexpr int TILE_ELEMS = kTileKeys * D;
-  constexpr int STAGE_ELEMS = 2 * TILE_ELEMS;        // K tile then V tile
+  // Staged tiles are row-major with padded rows instead of a swizzle, so
+  // every LDS read of a lane is one base address plus an immediate offset.
+  // K rows (D + 8 elements): the 16 lanes of a 16-byte read cover 64
+  // distinct banks.  V rows (D + 32 elements, 16 dwords mod 64 banks): the
+  // four keys that a transposed read's lane group touches fall in disjoint
+  // bank quarters.
+  constexpr int KROW = D + 8;
+  constexpr int VROW = D + 32;
+  constexpr int TILE_ELEMS = kTileKeys * KROW;       // V tile follows the K tile
+  constexpr int STAGE_ELEMS = kTileKeys * (KROW + VROW);
   constexpr int KCH = kTileKeys * CPR;               // chunks of one K (or V) tile
   constexpr int NCT = 2 * KCH / kRowsThreads;        // K+V chunks per thread per tile
-  constexpr int RING = D == 128 ? 6 : 8;
+  constexpr int NSTAGE = 3;
+  constexpr int RING = D == 128 ? 3 : 6;
   constexpr int NDB = D / 32;
   static_assert(NCT >= 1 && NCT * kRowsThreads == 2 * KCH, "tile must split evenly over the workgroup");
+  static_assert(RING % NSTAGE == 0, "a whole ring turn keeps LDS buffer indices compile-time");
 
-  __shared__ __attribute__((aligned(16))) T stage[2 * STAGE_ELEMS];
+  __shared__ __attribute__((aligned(16))) T stage[NSTAGE * STAGE_ELEMS];
   __shared__ uint32_t anc[GROWS][kAncWords];
   __shared__ int par[kMaxN];
 
@@ -710,13 +721,13 @@ void rows_kernel(PartialParams p) {
       rx[j] = buf_load16<NT>(isv ? vrs : krs, (isv ? vo : ko) + (uint32_t)col_t * 16u);
     }
   };
-  __shared__ int kval[2][kTileKeys];   // key of the staged tile exists
+  __shared__ int kval[NSTAGE][kTileKeys];   // key of the staged tile exists
   auto stage_write = [&](const u32x4 (&rx)[NCT], bool ok, int buf) __attribute__((always_inline)) {
     T* base = stage + buf * STAGE_ELEMS;
 #pragma unroll
     for (int j = 0; j < NCT; ++j) {
       const bool isv = 64 * wave_u + kRowsThreads * j >= KCH;
-      const int off = (isv ? TILE_ELEMS : 0) + kk_t * D + swz<CPR>(kk_t, col_t) * VEC;
+      const int off = isv ? TILE_ELEMS + kk_t * VROW + col_t * VEC : kk_t * KROW + col_t * VEC;
       *(u32x4*)(base + off) = rx[j];
     }
     if (tid < KCH && col_t == 0) kval[buf][kk_t] = ok;
@@ -730,22 +741,26 @@ void rows_kernel(PartialParams p) {
     for (int e = 0; e < 16; ++e) o[db][e] = 0.f;
   const float c = p.c;
 
-  auto compute = [&](int t, int buf, auto masked_tag) __attribute__((always_inline)) {
-    constexpr bool MASKED = decltype(masked_tag)::value;
+  // S^T of the tile staged in buffer buf
+  auto qk = [&](int buf) __attribute__((always_inline)) -> f32x16 {
     const T* kt = stage + buf * STAGE_ELEMS;
-    const T* vt = kt + TILE_ELEMS;
-    uint32_t key_bits = ~0u;
-    if constexpr (MASKED)
-      key_bits = (uint32_t)__ballot(kval[buf][n] != 0 && h == 0) & anc[32 * wave + n][t & (kAncWords - 1)];
-
     f32x16 s;
 #pragma unroll
     for (int e = 0; e < 16; ++e) s[e] = 0.f;
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) {
-      const u32x4 kv = *(const u32x4*)(kt + n * D + swz<CPR>(n, 2 * ks + h) * VEC);
+      const u32x4 kv = *(const u32x4*)(kt + n * KROW + (2 * ks + h) * VEC);
       s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kv), qop[ks], s, 0, 0, 0);
     }
+    return s;
+  };
+  // online softmax of tile t's scores s, then O^T += V^T P^T
+  auto soft_pv = [&](f32x16 s, int t, int buf, auto masked_tag) __attribute__((always_inline)) {
+    constexpr bool MASKED = decltype(masked_tag)::value;
+    const T* vt = stage + buf * STAGE_ELEMS + TILE_ELEMS;
+    uint32_t key_bits = ~0u;
+    if constexpr (MASKED)
+      key_bits = (uint32_t)__ballot(kval[buf][n] != 0 && h == 0) & anc[32 * wave + n][t & (kAncWords - 1)];
 
     float tmax = -INFINITY;
 #pragma unroll
@@ -756,7 +771,7 @@ void rows_kernel(PartialParams p) {
       }
       tmax = fmaxf(tmax, s[e]);
     }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+    tmax = half_max(tmax);
     const bool grow = (tmax - m_run) * c > 8.f;
     if (__any(grow)) {
       const float mnew = grow ? tmax : m_run;
@@ -791,7 +806,7 @@ void rows_kernel(PartialParams p) {
 #pragma unroll
         for (int rr = 0; rr < 2; ++rr) {
           const int key = 16 * ks + 8 * rr + 4 * h + (i16 >> 2);
-          const T* src = vt + key * D + swz<CPR>(key, d >> 3) * VEC + (d & 7);
+          const T* src = vt + key * VROW + d;
           typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
           const i16x4 tv = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)src);
           const u32x2 tw = __builtin_bit_cast(u32x2, tv);
@@ -803,65 +818,65 @@ void rows_kernel(PartialParams p) {
       }
     }
   };
-
-  // prologue: tiles 0..RING-1 in flight, tile 0 staged
+  // Software pipeline over three LDS stages: tiles t and t+1 are staged
+  // while tile t is processed, so the QK MFMAs of tile t+1 are issued
+  // before the softmax of tile t and run under it; then tile t+2 is staged
+  // into the buffer tile t-1 used.
+  // prologue: tiles 0..RING-1 in flight, tiles 0 and 1 staged, S of tile 0
 #pragma unroll
   for (int pp = 0; pp < RING; ++pp) {
     load(pp, load_idx(pp), rg[pp], okr[pp]);
     ixr[pp] = load_idx(pp + RING);
   }
-  stage_write(rg[0], okr[0], 0);
-  load(RING, ixr[0], rg[0], okr[0]);
-  ixr[0] = load_idx(2 * RING);
+#pragma unroll
+  for (int pp = 0; pp < 2; ++pp) {
+    stage_write(rg[pp], okr[pp], pp);
+    load(RING + pp, ixr[pp], rg[pp], okr[pp]);
+    ixr[pp] = load_idx(2 * RING + pp);
+  }
   lds_barrier();
-
-  // Tiles [0, t_end): compute tile t from LDS buffer t & 1, then stage tile
-  // t+1 from its ring slot and refill the slot with tile t+1+RING.  Each
-  // call site has one compute variant, so no loop body holds both.  The main
-  // loop takes whole turns of the ring with no early exit, which keeps the
-  // compiler's wait before each staged slot partial; the last turn (fewer
-  // than RING tiles, nothing left to load) follows it.
+  f32x16 s_cur = qk(0);
   auto tile_loop = [&](int t_end, auto masked_tag) __attribute__((always_inline)) {
     int t0 = 0;
     for (; t0 + RING <= t_end; t0 += RING) {
 #pragma unroll
       for (int pp = 0; pp < RING; ++pp) {
         const int t = t0 + pp;
-        compute(t, t & 1, masked_tag);
-        const int nx = (pp + 1) % RING;
-        stage_write(rg[nx], okr[nx], (t + 1) & 1);
-        load(t + 1 + RING, ixr[nx], rg[nx], okr[nx]);
-        ixr[nx] = load_idx(t + 1 + 2 * RING);
+        const f32x16 s_nxt = qk((t + 1) % NSTAGE);
+        soft_pv(s_cur, t, t % NSTAGE, masked_tag);
+        const int nx = (pp + 2) % RING;
+        stage_write(rg[nx], okr[nx], (t + 2) % NSTAGE);
+        load(t + 2 + RING, ixr[nx], rg[nx], okr[nx]);
+        ixr[nx] = load_idx(t + 2 + 2 * RING);
         lds_barrier();
+        s_cur = s_nxt;
       }
     }
 #pragma unroll
     for (int pp = 0; pp < RING - 1; ++pp) {
       const int t = t0 + pp;
       if (t < t_end) {
-        compute(t, t & 1, masked_tag);
-        const int nx = (pp + 1) % RING;
-        stage_write(rg[nx], okr[nx], (t + 1) & 1);
+        const f32x16 s_nxt = qk((t + 1) % NSTAGE);
+        soft_pv(s_cur, t, t % NSTAGE, masked_tag);
+        const int nx = (pp + 2) % RING;
+        stage_write(rg[nx], okr[nx], (t + 2) % NSTAGE);
         lds_barrier();
+        s_cur = s_nxt;
       }
     }
   };
-  if (tree) {
+  if (tree || gather) {
     tile_loop(ntiles, std::true_type{});
   } else {
-    // whole tiles without the mask, then the partial tail tile (already
-    // staged in buffer nfull & 1 by the loop) with it
+    // whole tiles without the mask, then the partial tail tile (staged in
+    // buffer nfull % NSTAGE, its S in s_cur) with it
     const int nfull = (ke - kb) / kTileKeys;
-    if (gather) {
-      tile_loop(ntiles, std::true_type{});
-    } else {
-      tile_loop(nfull, std::false_type{});
-      if (nfull < ntiles) compute(nfull, nfull & 1, std::true_type{});
-    }
+    tile_loop(nfull, std::false_type{});
+    if (nfull < ntiles) soft_pv(s_cur, nfull, nfull % NSTAGE, std::true_type{});
   }
 
   // this wavefront's rows: normalised partial and log2-sum-exp
-  const float l = l_run + __shfl_xor(l_run, 32);
+  const float l = half_sum(l_run);
   if (myrow < p.R) {
     const int g = myrow / p.N, i = myrow % p.N;
     const int64_t prow = ((int64_t)b * p.Hq + kvh * p.G + g) * p.N + i;

@@ -30,6 +30,27 @@ __device__ inline int xcd_remap(int x, int total) {
 
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Maximum and sum of x over lanes l and l ^ 32, through the cross-half lane
+// swap (a VALU operation, no LDS round trip).  Of the swap's two results, in
+// every lane one holds x of lanes 0-31 and the other x of lanes 32-63, so
+// both halves combine the same two values in the same order.
+__device__ inline void half_swap(float x, float& lo, float& hi) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x), __builtin_bit_cast(uint32_t, x),
+                                                  false, false);
+  lo = __builtin_bit_cast(float, (uint32_t)r[0]);
+  hi = __builtin_bit_cast(float, (uint32_t)r[1]);
+}
+__device__ inline float half_max(float x) {
+  float lo, hi;
+  half_swap(x, lo, hi);
+  return fmaxf(lo, hi);
+}
+__device__ inline float half_sum(float x) {
+  float lo, hi;
+  half_swap(x, lo, hi);
+  return lo + hi;
+}
+
 // Workgroup barrier for LDS hand-offs inside the streaming loops.
 // __syncthreads() is a workgroup release/acquire fence and waits for every
 // outstanding global load too, which would drain the register prefetch ring

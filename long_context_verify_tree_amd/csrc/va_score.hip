@@ -108,12 +108,12 @@ __global__ __launch_bounds__(kSThreads) void score_partial_kernel(ScoreParams p)
       s[e] = key < ke ? s[e] * c : -INFINITY;
       tmax = fmaxf(tmax, s[e]);
     }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+    tmax = half_max(tmax);
     const float mnew = fmaxf(m_run, tmax);
     float ls = 0.f;
 #pragma unroll
     for (int e = 0; e < 16; ++e) ls += fast_exp2(s[e] - mnew);
-    ls += __shfl_xor(ls, 32);
+    ls = half_sum(ls);
     l_run = (m_run == -INFINITY ? 0.f : l_run * fast_exp2(m_run - mnew)) + ls;
     m_run = mnew;
     if (n < p.M) {
