@@ -67,7 +67,11 @@ def committed_traffic(kernel: str, workload: str):
         if ":" in line and line.startswith("- "):
             k, v = line[2:].split(":", 1)
             fields[k.strip()] = v.strip().strip("`")
-    digest = hashlib.sha256(open(os.path.join(CSRC, KERNEL_SOURCES[kernel]), "rb").read()).hexdigest()
+    # the kernel's source file, then the device header every kernel includes
+    h = hashlib.sha256()
+    for name in (KERNEL_SOURCES[kernel], "va_device.h"):
+        h.update(open(os.path.join(CSRC, name), "rb").read())
+    digest = h.hexdigest()
     if fields.get("kernel source sha256") != digest or "traffic bytes per launch" not in fields:
         return None, os.path.relpath(path, ROOT) + " (stale: kernel changed since the counters were taken)"
     return int(float(fields["traffic bytes per launch"])), os.path.relpath(path, ROOT)
