@@ -7,8 +7,10 @@
 // the softmax taken over the L context tokens.  A row's softmax needs its
 // log-sum-exp over all of L before any probability is final, so the work is
 // two kernels:
-//   score_partial_kernel  one workgroup per (sequence, head, split of L):
-//                         S^T = K_tile . Q^T on MFMA for up to 32 rows,
+//   score_partial_kernel  one workgroup per (sequence, head, split of L);
+//                         each wavefront keeps two K tiles in flight in
+//                         registers; S^T = K_tile . Q^T on MFMA for up to
+//                         32 rows,
 //                         writes the scaled scores (log2 domain) to the
 //                         workspace and each row's (max, sum) of the split;
 //   score_finish_kernel   one workgroup per (sequence, 1024 tokens): merges
@@ -77,20 +79,28 @@ __global__ __launch_bounds__(kSThreads) void score_partial_kernel(ScoreParams p)
 
   float m_run = -INFINITY, l_run = 0.f;
   const float c = p.c;
-  u32x4 kr[NCH];
-  auto load = [&](int t) __attribute__((always_inline)) {
+  // Wave w takes tiles w, w + 4, ...: its i-th tile is w + 4 i.  A ring of
+  // two register tiles keeps the next two in flight while one is used;
+  // slots past the part's last tile load nothing (out-of-range offset).
+  constexpr int RING = 2;
+  const int nt_w = ntiles > wave ? (ntiles - wave + kSWavesS - 1) / kSWavesS : 0;
+  u32x4 kr[RING][NCH];
+  auto load = [&](u32x4 (&rx)[NCH], int i) __attribute__((always_inline)) {
+    const int t = wave + kSWavesS * i;
 #pragma unroll
-    for (int cc = 0; cc < NCH; ++cc)
-      kr[cc] = buf_load16<true>(krs, (uint32_t)(kb + kSTile * t + kk0 + KPC * cc) * kts_b + col_b);   // past L: zeros
+    for (int cc = 0; cc < NCH; ++cc) {
+      const uint32_t off = (uint32_t)(kb + kSTile * t + kk0 + KPC * cc) * kts_b + col_b;
+      rx[cc] = buf_load16<true>(krs, i < nt_w ? off : kOOB);   // past L: zeros
+    }
   };
-  if (wave < ntiles) load(wave);
-  for (int t = wave; t < ntiles; t += kSWavesS) {
+  auto process = [&](u32x4 (&rx)[NCH], int i) __attribute__((always_inline)) {
+    const int t = wave + kSWavesS * i;
 #pragma unroll
     for (int cc = 0; cc < NCH; ++cc) {
       const int kk = kk0 + KPC * cc;
-      *(u32x4*)(kt + kk * D + swz<CPR>(kk, lane % CPR) * VEC) = kr[cc];
+      *(u32x4*)(kt + kk * D + swz<CPR>(kk, lane % CPR) * VEC) = rx[cc];
     }
-    if (t + kSWavesS < ntiles) load(t + kSWavesS);   // next tile in flight during this one
+    load(rx, i + RING);   // refill the slot while this tile is used
     f32x16 s;
 #pragma unroll
     for (int e = 0; e < 16; ++e) s[e] = 0.f;
@@ -121,7 +131,16 @@ __global__ __launch_bounds__(kSThreads) void score_partial_kernel(ScoreParams p)
       for (int g = 0; g < 4; ++g)
         *(float4*)(srow + key0 + 8 * g + 4 * h) = make_float4(s[4 * g], s[4 * g + 1], s[4 * g + 2], s[4 * g + 3]);
     }
+  };
+#pragma unroll
+  for (int r = 0; r < RING; ++r) load(kr[r], r);
+  // whole turns of the ring (no early exit inside), then the odd last tile
+  int i = 0;
+  for (; i + RING <= nt_w; i += RING) {
+#pragma unroll
+    for (int r = 0; r < RING; ++r) process(kr[r], i + r);
   }
+  if (i < nt_w) process(kr[0], i);
   // the four wavefronts' (max, sum) of each row, in a fixed order
   if (h == 0) {
     mbuf[wave][n] = m_run;
