@@ -5,8 +5,9 @@ batch, through the C ABI: the partial kernel (context splits + tree part) and
 the log-sum-exp merge; for a sparse workload the step also runs the verify-set
 selector.  Inputs are seeded synthetic tensors of the workload's shape
 (long_context_verify_tree_amd.synth), resident in HBM before timing starts;
-several copies are rotated so no step can reuse the previous step's data from
-the 256 MB MALL.
+at least four copies are rotated, and enough that a copy is read again only
+after more than twice the 256 MB MALL of other inputs, so no step reuses
+cached data.
 
 Prints one JSON line.  `value` is the algorithmic HBM throughput of the whole
 step in GB/s (bytes the method must move / step time); the same line carries
@@ -387,8 +388,13 @@ def main():
     if sparse:
         base["draft_score"] = dv(x.draft_score, synth.FP32)
         base["target_score"] = dv(x.target_score, synth.FP32)
-    a_bytes_kv = 2 * cfg.B * cfg.Hkv * cfg.L * cfg.D * (4 if cfg.dtype == "fp32" else 2)
-    copies = args.copies or max(2, min(8, int(np.ceil(1.2e9 / max(a_bytes_kv, 1)))))
+    # Bytes one step reads from its input copy (gathered rows and scores when
+    # sparse).  At least four copies rotate, and enough that a copy is read
+    # again only after more than twice the 256 MB MALL of other inputs.
+    es = 4 if cfg.dtype == "fp32" else 2
+    n_keys = min(cfg.budget, cfg.L) if sparse else cfg.L
+    step_read = 2 * cfg.B * cfg.Hkv * n_keys * cfg.D * es + (2 * cfg.B * cfg.L * 4 if sparse else 0)
+    copies = args.copies or int(min(16, max(4, 1 + np.ceil(512e6 / max(step_read, 1)))))
     sets = [base] + [{k: v.clone() for k, v in base.items()} for _ in range(copies - 1)]
 
     n_ctx = min(cfg.budget, cfg.L) if sparse else cfg.L
