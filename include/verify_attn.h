@@ -268,7 +268,9 @@ va_status va_select_workspace_size(int32_t B, int32_t L, size_t* bytes);
  *   sink, window, top_m >= 0; budget >= min(L, |[0,sink) U [L-window,L)|)
  *   verify_idx  [B, min(budget, L)] int32, contiguous; ascending, distinct
  *   ws          device workspace of va_select_workspace_size(B, L) bytes
- * budget >= L returns every index 0..L-1. */
+ * budget >= L returns every index 0..L-1.  With budget < L, rows longer
+ * than 786432 tokens (24 x 32768) return VA_EUNSUPPORTED: each row's token
+ * marks are kept on chip. */
 va_status select_verify_set(const float* draft_score, const float* target_score,
                             int32_t B, int32_t L, int64_t ld,
                             int32_t sink, int32_t window, int32_t top_m, int32_t budget,

@@ -8,9 +8,11 @@
 
 namespace va {
 
-// Longest score row the selector handles: its token bitmap lives in LDS
-// (L / 8 bytes, at most 128 KiB of the 160 KiB per CU).
-constexpr int32_t kSelectMaxL = 1 << 20;
+// Longest score row the selector handles.  The kernel keeps one mark word
+// per thread and 32768-token segment in LDS (4 KiB per segment) beside about
+// 48 KiB of histograms; 24 segments keep the total within a CU's 160 KiB.
+constexpr int32_t kSelectSegTokens = 32768;
+constexpr int32_t kSelectMaxL = 24 * kSelectSegTokens;
 
 size_t select_ws_bytes(int32_t B, int32_t L);
 

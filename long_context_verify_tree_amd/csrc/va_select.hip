@@ -37,6 +37,7 @@ constexpr int kST = 1024;                 // threads per workgroup
 constexpr int kSWaves = kST / 64;
 constexpr int kKPT = 32;                  // tokens per thread per segment
 constexpr int kSeg = kST * kKPT;          // tokens per segment
+static_assert(kSeg == kSelectSegTokens, "segment size of the length limit");
 
 struct SelParams {
   const float* ds;
@@ -54,7 +55,9 @@ __device__ inline uint32_t order_key(float f) {
 }
 
 // Exclusive prefix sum of v over the workgroup in thread order; *total gets
-// the sum.  Uses wsum[kSWaves]; two barriers.
+// the sum.  Uses wsum[kSWaves]; two barriers, or one with TAIL = false when
+// the caller reaches another barrier before wsum is written again.
+template <bool TAIL = true>
 __device__ inline int block_excl_scan(int v, int* wsum, int* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int x = v;
@@ -72,7 +75,7 @@ __device__ inline int block_excl_scan(int v, int* wsum, int* total) {
     before += w < wave ? c : 0;
     tot += c;
   }
-  __syncthreads();
+  if (TAIL) __syncthreads();
   *total = tot;
   return before + x - v;
 }
@@ -84,7 +87,8 @@ constexpr int kBins0 = 1 << 12;
 
 struct SelShared {
   int hist_d[kBins0];        // first-digit histogram of the draft tier
-  int hist_t[kBins0];        // first-digit histogram of the target tier; later digits reuse hist_d
+  int hist_t[kBins0];        // first-digit histogram of the target tier
+  int hist_p[2][2][1 << 10]; // [tier][pass - 1]: later digits, zeroed with the others at the start
   int wsum[kSWaves];
   int pick[2];               // digit, candidates in higher buckets
 };
@@ -100,8 +104,8 @@ __device__ inline uint32_t range_bits(int j0, int lo, int hi) {
 // Given a histogram of `nbins` buckets (nbins / kST per thread, highest
 // buckets at the lowest threads) and `above` candidates in higher buckets
 // already, finds the bucket holding the r-th largest candidate: sets
-// sh.pick = {bucket, candidates above it}.  Three barriers; every thread
-// reads the result after the last.
+// sh.pick = {bucket, candidates above it}.  Two barriers; every thread
+// reads the result after the last, which also orders the next use of wsum.
 __device__ inline void pick_bucket(const int* hist, int nbins, int r, int above, SelShared& sh) {
   const int tid = threadIdx.x;
   const int per = nbins / kST;   // 4 or 1
@@ -113,7 +117,7 @@ __device__ inline void pick_bucket(const int* hist, int nbins, int r, int above,
     csum += c[k];
   }
   int tot;
-  int cum = above + block_excl_scan(csum, sh.wsum, &tot);
+  int cum = above + block_excl_scan<false>(csum, sh.wsum, &tot);
   if (cum < r && cum + csum >= r) {
     int bucket = top - 1;
     for (int k = 0; k < per; ++k) {
@@ -128,6 +132,9 @@ __device__ inline void pick_bucket(const int* hist, int nbins, int r, int above,
   }
   __syncthreads();
 }
+
+static_assert(sizeof(SelShared) + (size_t)(kSelectMaxL / kSeg) * kST * sizeof(uint32_t) <= 160 * 1024,
+              "histograms and the mark words of the longest row must fit in LDS");
 
 template <bool RESIDENT>
 __global__ __launch_bounds__(kST) void select_kernel(SelParams p) {
@@ -158,6 +165,7 @@ __global__ __launch_bounds__(kST) void select_kernel(SelParams p) {
   for (int i = tid; i < kBins0; i += kST) {
     sh.hist_d[i] = 0;
     sh.hist_t[i] = 0;
+    (&sh.hist_p[0][0][0])[i] = 0;
   }
 
   uint32_t kd[kKPT], kt[kKPT];
@@ -207,7 +215,8 @@ __global__ __launch_bounds__(kST) void select_kernel(SelParams p) {
 
   // Marks the top r candidates (free tokens not yet marked) of a tier whose
   // first-digit histogram is hist0; key holds the keys when resident.
-  auto tier = [&](const float* row, int r, int* hist0, uint32_t (&key)[kKPT]) __attribute__((always_inline)) {
+  auto tier = [&](const float* row, int r, int* hist0, int (&histp)[2][1 << 10], uint32_t (&key)[kKPT])
+                  __attribute__((always_inline)) {
     uint32_t prefix = 0;
     int above = 0;
     pick_bucket(hist0, kBins0, r, 0, sh);
@@ -217,20 +226,18 @@ __global__ __launch_bounds__(kST) void select_kernel(SelParams p) {
       const int shift = kDigitShift[pass];
       const int nb = 1 << kDigitBits[pass];
       const int hs = shift + kDigitBits[pass];   // bits above this digit are fixed
-      __syncthreads();   // everyone has read pick before the histogram is reused
-      for (int i = tid; i < nb; i += kST) sh.hist_d[i] = 0;
-      __syncthreads();
+      int* hist = histp[pass - 1];               // zeroed at the start
       for (int s = 0; s < nseg; ++s) {
         if (!RESIDENT) load_keys(row, s, key);
         const uint32_t cand = free_bits(s) & ~marks[s * kST + tid];
 #pragma unroll
         for (int i = 0; i < kKPT; ++i) {
           if (((cand >> i) & 1u) && (key[i] >> hs) == (prefix >> hs))
-            atomicAdd(&sh.hist_d[(key[i] >> shift) & (uint32_t)(nb - 1)], 1);
+            atomicAdd(&hist[(key[i] >> shift) & (uint32_t)(nb - 1)], 1);
         }
       }
       __syncthreads();
-      pick_bucket(sh.hist_d, nb, r, above, sh);
+      pick_bucket(hist, nb, r, above, sh);
       prefix |= (uint32_t)sh.pick[0] << shift;
       above = sh.pick[1];
     }
@@ -259,7 +266,7 @@ __global__ __launch_bounds__(kST) void select_kernel(SelParams p) {
     }
   };
 
-  if (r1 > 0) tier(ds, r1, sh.hist_d, kd);
+  if (r1 > 0) tier(ds, r1, sh.hist_d, sh.hist_p[0], kd);
   if (r2 > 0) {
     if (r1 > 0) {
       // take the draft tier's picks out of the target histogram
@@ -272,7 +279,7 @@ __global__ __launch_bounds__(kST) void select_kernel(SelParams p) {
       }
       __syncthreads();
     }
-    tier(ts, r2, sh.hist_t, kt);
+    tier(ts, r2, sh.hist_t, sh.hist_p[1], kt);
   }
 
   // ascending output: sink, both tiers and window

@@ -156,7 +156,9 @@ def test_select_rejects_before_launch(ops):
     assert select(ops, 2, 1000, 1000, -1, 16, 10, 100) == ops.VA_EINVAL
     assert select(ops, 2, 1000, 1000, 4, 16, 10, 100, out=None) == ops.VA_EINVAL
     assert select(ops, 2, 1000, 1000, 4, 16, 10, 100, ds=None) == ops.VA_EINVAL
-    assert select(ops, 1, (1 << 20) + 1, (1 << 20) + 1, 4, 16, 10, 100) == ops.VA_EUNSUPPORTED
+    longest = 24 * 32768                                                          # longest selector row
+    assert select(ops, 1, longest + 1, longest + 1, 4, 16, 10, 100) == ops.VA_EUNSUPPORTED
+    assert select(ops, 1, longest + 1, longest + 1, 4, 16, 10, longest + 1, out=None) == ops.VA_EINVAL  # all taken: no limit
     # nothing to do: OK without a launch
     assert select(ops, 0, 1000, 1000, 4, 16, 10, 100) == ops.VA_OK
     assert select(ops, 2, 1000, 1000, 4, 16, 10, 0, out=None) != ops.VA_EHIP

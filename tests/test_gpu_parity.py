@@ -259,6 +259,13 @@ def test_selector_ties_specials_and_special_cases(gpu_lib):
         torch.cuda.synchronize()
         np.testing.assert_array_equal(g.cpu().numpy(), vo.select_verify_set(d, t, S, W, m, budget),
                                       err_msg=str((S, W, m, budget)))
+    say("case selector longest row (24 segments)")
+    # the row length limit: every segment's marks and the histograms fit in LDS
+    Lmax = 24 * 32768
+    d = rng.lognormal(0, 2, (1, Lmax)).astype(np.float32)
+    t = rng.lognormal(0, 2, (1, Lmax)).astype(np.float32)
+    got = _sel_gpu(gpu_lib, d, t, 4, 256, 2048, 4096)
+    np.testing.assert_array_equal(got, vo.select_verify_set(d, t, 4, 256, 2048, 4096))
     say("case selector lognormal ragged")
     for L in (1, 31, 1025, 4099):
         d = rng.lognormal(0, 2, (2, L)).astype(np.float32)
