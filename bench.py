@@ -403,6 +403,8 @@ def main():
     desc = ops.make_desc(base["q"], base["k_cache"], base["v_cache"], base["k_draft"], base["v_draft"], out)
     ws = torch.empty(ops.workspace_size(desc, n_ctx), dtype=torch.uint8, device=dev)
     idx_bufs = [torch.empty(cfg.B, n_ctx, dtype=torch.int32, device=dev) for _ in sets] if sparse else None
+    sel_ws = (torch.empty(max(ops.select_workspace_size(cfg.B, cfg.L), 1), dtype=torch.uint8, device=dev)
+              if sparse else None)
 
     def step(i, ev=None):
         s = sets[i % len(sets)]
@@ -411,7 +413,8 @@ def main():
         idx = None
         if sparse:
             idx = ops.select_verify_set(s["draft_score"], s["target_score"], sink=cfg.sink, window=cfg.window,
-                                        top_m=cfg.top_m, budget=cfg.budget, out=idx_bufs[i % len(sets)])
+                                        top_m=cfg.top_m, budget=cfg.budget, out=idx_bufs[i % len(sets)],
+                                        workspace=sel_ws)
         if ev is not None:
             ev[1].record()
         ops.verify_attn_partials(desc, s["q"], s["k_cache"], s["v_cache"], s["k_draft"], s["v_draft"],

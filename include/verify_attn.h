@@ -260,7 +260,10 @@ va_status accept_commit(const va_attn_desc* desc, void* k_cache, void* v_cache,
                         const int32_t* accepted, const int32_t* cache_len, int32_t* new_len,
                         void* stream);
 
-/* Workspace bytes needed by select_verify_set for B rows of L scores. */
+/* Workspace bytes needed by select_verify_set for B rows of L scores
+ * (zero when each row runs in one workgroup; rows longer than 32768 tokens
+ * of a small batch are split over several workgroups that meet through the
+ * workspace).  Calls that overlap in time must not share a workspace. */
 va_status va_select_workspace_size(int32_t B, int32_t L, size_t* bytes);
 
 /* Verify-set selection.

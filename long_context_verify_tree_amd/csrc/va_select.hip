@@ -22,7 +22,9 @@
 // A last block scan of the per-thread mark counts (plus sink and window)
 // writes the ascending index list.  A row of one segment keeps its keys in
 // registers for all passes; longer rows re-read each segment per pass (the
-// row then sits in L2).
+// row then sits in L2).  Rows longer than one segment go to a second kernel
+// instead (select_cluster_kernel, below) when the batch is small enough:
+// several workgroups per row, each holding 8192 tokens in registers.
 
 #include <stdint.h>
 
@@ -57,7 +59,7 @@ __device__ inline uint32_t order_key(float f) {
 // Exclusive prefix sum of v over the workgroup in thread order; *total gets
 // the sum.  Uses wsum[kSWaves]; two barriers, or one with TAIL = false when
 // the caller reaches another barrier before wsum is written again.
-template <bool TAIL = true>
+template <bool TAIL = true, int NW = kSWaves>
 __device__ inline int block_excl_scan(int v, int* wsum, int* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int x = v;
@@ -70,7 +72,7 @@ __device__ inline int block_excl_scan(int v, int* wsum, int* total) {
   __syncthreads();
   int before = 0, tot = 0;
 #pragma unroll
-  for (int w = 0; w < kSWaves; ++w) {
+  for (int w = 0; w < NW; ++w) {
     const int c = wsum[w];
     before += w < wave ? c : 0;
     tot += c;
@@ -300,13 +302,274 @@ __global__ __launch_bounds__(kST) void select_kernel(SelParams p) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Multi-workgroup selection.  A row of P >= 2 segments of kCSeg tokens is
+// split over P workgroups of kCT threads, one per segment; each holds its
+// segment's keys in registers (thread t: tokens 32t .. 32t+31 of the
+// segment, as above) and runs the same steps as select_kernel.  The
+// workgroups of a row meet at row barriers, where
+//   * the histograms of each radix pass are summed in the row's workspace
+//     (integer atomics of each workgroup's nonzero LDS bins), and every
+//     workgroup reads the sums back and takes the same bucket;
+//   * the counts of equal keys and of output tokens are published per
+//     segment, so each workgroup knows how many precede it in index order.
+// A row barrier is an arrival counter in the workspace: each workgroup adds
+// one and waits until all P have arrived for this phase.  The wait is
+// bounded (a flag in the workspace records a timeout), so every wave exits;
+// the launch is used only when all B * P workgroups fit on the device at
+// once, which the waits rely on.
+
+constexpr int kCT = 256;                   // threads per workgroup
+constexpr int kCWaves = kCT / 64;
+constexpr int kCSeg = kCT * kKPT;          // 8192 tokens per workgroup
+constexpr int kCMaxGroups = 512;           // B * P limit: every workgroup resident
+constexpr int kSpinLimit = 1 << 18;        // polls per wait (each a device-coherent load: < 1 s)
+
+// Workspace of one row, in ints, zeroed before the launch.
+constexpr int kWsHd = 0;                   // first digit, draft tier [kBins0]
+constexpr int kWsHt = kBins0;              // first digit, target tier [kBins0]
+constexpr int kWsHp = 2 * kBins0;          // later digits [tier][pass - 1][1024]
+constexpr int kWsBar = kWsHp + 4 * 1024;   // arrival counter
+constexpr int kWsErr = kWsBar + 1;         // set when a wait timed out
+constexpr int kWsCnt = kWsBar + 64;        // per segment: equal keys [2][P], output tokens [P]
+
+__host__ __device__ inline int64_t cluster_row_ints(int P) { return ((int64_t)kWsCnt + 3 * P + 63) / 64 * 64; }
+
+struct CShared {
+  int ha[kBins0];     // a workgroup histogram, then the row's sums for a pick
+  int hb[kBins0];
+  int wsum[kCWaves];
+  int pick[2];
+};
+
+__device__ inline int ld_dev(const int* p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+
+// Returns once every workgroup of the row has reached its `phase`-th
+// barrier (or the wait timed out).  Everything the workgroups exchange is
+// written with agent-scope atomics (performed where every XCD sees them) and
+// read with agent-scope loads, so no cache write-back or invalidation is
+// needed: each wavefront only waits until its own atomics are performed
+// before the workgroup arrives.
+__device__ inline void row_barrier(int* ws, int P, int phase) {
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    __hip_atomic_fetch_add(ws + kWsBar, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int target = phase * P;
+    for (int spin = 0; ld_dev(ws + kWsBar) < target; ++spin) {
+      if (spin == kSpinLimit) {
+        __hip_atomic_store(ws + kWsErr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+    }
+  }
+  __syncthreads();
+}
+
+// pick_bucket for a workgroup of kCT threads: nbins / kCT buckets per
+// thread, highest at the lowest threads.  Two barriers.
+__device__ inline void cpick(const int* hist, int nbins, int r, int above, CShared& sh) {
+  const int tid = threadIdx.x;
+  const int per = nbins / kCT;   // 16 or 4
+  const int top = nbins - per * tid;
+  int csum = 0;
+  for (int k = 0; k < per; ++k) csum += hist[top - 1 - k];
+  int tot;
+  const int cum0 = above + block_excl_scan<false, kCWaves>(csum, sh.wsum, &tot);
+  if (cum0 < r && cum0 + csum >= r) {
+    int cum = cum0, bucket = top - 1;
+    for (int k = 0; k < per; ++k) {
+      const int ck = hist[top - 1 - k];
+      if (cum + ck >= r) {
+        bucket = top - 1 - k;
+        break;
+      }
+      cum += ck;
+    }
+    sh.pick[0] = bucket;
+    sh.pick[1] = cum;
+  }
+  __syncthreads();
+}
+
+__global__ __launch_bounds__(kCT) void select_cluster_kernel(SelParams p, int* ws_all, int P) {
+  __shared__ CShared sh;
+  const int tid = threadIdx.x;
+  const int b = blockIdx.x / P, seg = blockIdx.x % P;
+  int* ws = ws_all + (int64_t)b * cluster_row_ints(P);
+  const float* ds = p.ds + (int64_t)b * p.ld;
+  const float* ts = p.ts + (int64_t)b * p.ld;
+  int32_t* out = p.out + (int64_t)b * p.k_out;
+  const int L = p.L;
+  const int lo = p.sink < L ? p.sink : L;
+  const int w = p.window < L ? p.window : L;
+  const int hi = L - w > lo ? L - w : lo;
+  const int n_prot = lo + (L - hi);
+  const int rest = p.budget - n_prot;
+  const int n_free = hi - lo;
+  int r1 = p.top_m < rest ? p.top_m : rest;
+  r1 = r1 < n_free ? r1 : n_free;
+  const int r2 = rest - r1;
+  const int j0 = seg * kCSeg + tid * kKPT;
+
+  uint32_t kd[kKPT], kt[kKPT];
+  auto load_keys = [&](const float* row, uint32_t (&key)[kKPT]) __attribute__((always_inline)) {
+    const bool vec = j0 + kKPT <= L && ((reinterpret_cast<uintptr_t>(row + j0) & 15u) == 0);
+    if (vec) {
+#pragma unroll
+      for (int q = 0; q < kKPT / 4; ++q) {
+        const float4 v = *reinterpret_cast<const float4*>(row + j0 + 4 * q);
+        key[4 * q + 0] = order_key(v.x);
+        key[4 * q + 1] = order_key(v.y);
+        key[4 * q + 2] = order_key(v.z);
+        key[4 * q + 3] = order_key(v.w);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < kKPT; ++i) key[i] = j0 + i < L ? order_key(row[j0 + i]) : 0u;
+    }
+  };
+  load_keys(ds, kd);
+  load_keys(ts, kt);
+  const uint32_t free = range_bits(j0, lo, hi);
+  uint32_t mark = 0;
+  int phase = 0;
+
+  // first digit of both tiers; the target histogram counts every free token
+  // and is corrected for the draft tier's picks later
+  for (int i = tid; i < kBins0; i += kCT) {
+    sh.ha[i] = 0;
+    sh.hb[i] = 0;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < kKPT; ++i) {
+    if ((free >> i) & 1u) {
+      if (r1 > 0) atomicAdd(&sh.ha[kd[i] >> kDigitShift[0]], 1);
+      if (r2 > 0) atomicAdd(&sh.hb[kt[i] >> kDigitShift[0]], 1);
+    }
+  }
+  __syncthreads();
+  for (int i = tid; i < kBins0; i += kCT) {
+    if (sh.ha[i]) atomicAdd(ws + kWsHd + i, sh.ha[i]);
+    if (sh.hb[i]) atomicAdd(ws + kWsHt + i, sh.hb[i]);
+  }
+  row_barrier(ws, P, ++phase);
+
+  // Marks the top r candidates (free, not yet marked) of tier ti, whose
+  // row-wide first-digit histogram is g0.
+  auto tier = [&](int ti, int r, const int* g0, uint32_t (&key)[kKPT]) __attribute__((always_inline)) {
+    for (int i = tid; i < kBins0; i += kCT) sh.ha[i] = ld_dev(g0 + i);
+    __syncthreads();
+    cpick(sh.ha, kBins0, r, 0, sh);
+    uint32_t prefix = (uint32_t)sh.pick[0] << kDigitShift[0];
+    int above = sh.pick[1];
+    for (int pass = 1; pass < 3; ++pass) {
+      const int shift = kDigitShift[pass];
+      const int nb = 1 << kDigitBits[pass];
+      const int hs = shift + kDigitBits[pass];   // bits above this digit are fixed
+      int* gp = ws + kWsHp + (2 * ti + pass - 1) * 1024;
+      for (int i = tid; i < nb; i += kCT) sh.hb[i] = 0;
+      __syncthreads();
+      const uint32_t cand = free & ~mark;
+#pragma unroll
+      for (int i = 0; i < kKPT; ++i) {
+        if (((cand >> i) & 1u) && (key[i] >> hs) == (prefix >> hs))
+          atomicAdd(&sh.hb[(key[i] >> shift) & (uint32_t)(nb - 1)], 1);
+      }
+      __syncthreads();
+      for (int i = tid; i < nb; i += kCT)
+        if (sh.hb[i]) atomicAdd(gp + i, sh.hb[i]);
+      row_barrier(ws, P, ++phase);
+      for (int i = tid; i < nb; i += kCT) sh.ha[i] = ld_dev(gp + i);
+      __syncthreads();
+      cpick(sh.ha, nb, r, above, sh);
+      prefix |= (uint32_t)sh.pick[0] << shift;
+      above = sh.pick[1];
+    }
+    // every candidate above T, and the first (r - above) equal to T in
+    // index order over the whole row
+    const uint32_t T = prefix;
+    const int need_eq = r - above;
+    const uint32_t cand = free & ~mark;
+    uint32_t gt = 0, eq = 0;
+#pragma unroll
+    for (int i = 0; i < kKPT; ++i) {
+      const bool c = (cand >> i) & 1u;
+      gt |= (uint32_t)(c && key[i] > T) << i;
+      eq |= (uint32_t)(c && key[i] == T) << i;
+    }
+    int tot;
+    const int before = block_excl_scan<true, kCWaves>(__popc(eq), sh.wsum, &tot);
+    if (tid == 0) __hip_atomic_store(ws + kWsCnt + ti * P + seg, tot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    row_barrier(ws, P, ++phase);
+    int prev = 0;   // equal keys in earlier segments
+    for (int q = tid; q < seg; q += kCT) prev += ld_dev(ws + kWsCnt + ti * P + q);
+    int earlier;
+    block_excl_scan<true, kCWaves>(prev, sh.wsum, &earlier);
+    int take = need_eq - earlier - before;
+    uint32_t eq_taken = 0;
+    for (uint32_t e = eq; e && take > 0; e &= e - 1, --take) eq_taken |= e & (~e + 1u);
+    mark |= gt | eq_taken;
+  };
+
+  if (r1 > 0) tier(0, r1, ws + kWsHd, kd);
+  if (r2 > 0) {
+    if (r1 > 0) {
+      // take the draft tier's picks out of the target histogram
+#pragma unroll
+      for (int i = 0; i < kKPT; ++i)
+        if ((mark >> i) & 1u) atomicSub(ws + kWsHt + (kt[i] >> kDigitShift[0]), 1);
+      row_barrier(ws, P, ++phase);
+    }
+    tier(1, r2, ws + kWsHt, kt);
+  }
+
+  // ascending output: sink, both tiers and window
+  const uint32_t valid = range_bits(j0, 0, L);
+  const uint32_t sel = (mark | (valid & ~free)) & valid;
+  int tot;
+  const int before = block_excl_scan<true, kCWaves>(__popc(sel), sh.wsum, &tot);
+  if (tid == 0) __hip_atomic_store(ws + kWsCnt + 2 * P + seg, tot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  row_barrier(ws, P, ++phase);
+  int prev = 0;
+  for (int q = tid; q < seg; q += kCT) prev += ld_dev(ws + kWsCnt + 2 * P + q);
+  int earlier;
+  block_excl_scan<true, kCWaves>(prev, sh.wsum, &earlier);
+  int pos = earlier + before;
+  for (uint32_t e = sel; e; e &= e - 1) {
+    const int i = __ffs(e) - 1;
+    if (pos < p.k_out) out[pos] = j0 + i;
+    ++pos;
+  }
+}
+
+__global__ __launch_bounds__(256) void zero_ints_kernel(int* p, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = 0;
+}
+
+// Rows that the multi-workgroup kernel takes: budget < L (checked by the
+// caller), longer than one segment of select_kernel (which keeps a
+// one-segment row in registers, while longer rows are re-read on every pass;
+// a row barrier costs a few microseconds), and every workgroup resident at
+// once.  Measured: 16 rows of 32768 tokens 36 us in select_kernel, 53 us
+// here; 4 rows of 131072 tokens 178 us there, 58 us here.
+inline int cluster_parts(int32_t B, int32_t L) {
+  const int P = (int)(((int64_t)L + kCSeg - 1) / kCSeg);
+  return L > kSeg && (int64_t)B * P <= kCMaxGroups ? P : 0;
+}
+
 }  // namespace
 
-size_t select_ws_bytes(int32_t, int32_t) { return 0; }
+size_t select_ws_bytes(int32_t B, int32_t L) {
+  const int P = cluster_parts(B, L);
+  return P ? (size_t)B * cluster_row_ints(P) * sizeof(int) : 0;
+}
 
 hipError_t launch_select(const float* draft_score, const float* target_score, int32_t B, int32_t L, int64_t ld,
                          int32_t sink, int32_t window, int32_t top_m, int32_t budget, int32_t* verify_idx,
-                         void*, hipStream_t stream) {
+                         void* ws, hipStream_t stream) {
   SelParams p{};
   p.ds = draft_score;
   p.ts = target_score;
@@ -318,6 +581,16 @@ hipError_t launch_select(const float* draft_score, const float* target_score, in
   p.top_m = top_m;
   p.budget = budget;
   p.k_out = budget < L ? budget : L;
+  const int P = budget < L ? cluster_parts(B, L) : 0;
+  if (P) {
+    const int64_t n = (int64_t)B * cluster_row_ints(P);
+    const int grid = (int)((n + 255) / 256 < 1024 ? (n + 255) / 256 : 1024);
+    hipLaunchKernelGGL(zero_ints_kernel, dim3(grid), dim3(256), 0, stream, (int*)ws, n);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(select_cluster_kernel, dim3(B * P), dim3(kCT), 0, stream, p, (int*)ws, P);
+    return hipGetLastError();
+  }
   const int nseg = (L + kSeg - 1) / kSeg;
   const size_t lds = (size_t)(nseg > 0 ? nseg : 1) * kST * sizeof(uint32_t);
   const bool resident = nseg <= 1;

@@ -254,7 +254,10 @@ def test_selector_ties_specials_and_special_cases(gpu_lib):
     dpad[:, :L2] = torch.from_numpy(d)
     tpad[:, :L2] = torch.from_numpy(t)
     dv, tv = dpad.cuda()[:, :L2], tpad.cuda()[:, :L2]
-    for (S, W, m, budget) in ((4, 256, 1024, 2048), (4, 256, 20000, 30000), (0, 100, 5, 9000)):
+    # (rows of more than one 32768-token segment run on several workgroups per
+    # row; the last three skip the draft tier, the target tier, and both)
+    for (S, W, m, budget) in ((4, 256, 1024, 2048), (4, 256, 20000, 30000), (0, 100, 5, 9000),
+                              (4, 256, 0, 5000), (4, 256, 50000, 3000), (4, 256, 10, 260)):
         g = gpu_lib.select_verify_set(dv, tv, sink=S, window=W, top_m=m, budget=budget)
         torch.cuda.synchronize()
         np.testing.assert_array_equal(g.cpu().numpy(), vo.select_verify_set(d, t, S, W, m, budget),
@@ -266,6 +269,14 @@ def test_selector_ties_specials_and_special_cases(gpu_lib):
     t = rng.lognormal(0, 2, (1, Lmax)).astype(np.float32)
     got = _sel_gpu(gpu_lib, d, t, 4, 256, 2048, 4096)
     np.testing.assert_array_equal(got, vo.select_verify_set(d, t, 4, 256, 2048, 4096))
+    say("case selector wide batch of long rows (one workgroup per row)")
+    # 8 rows x 19 segments: more workgroups than the multi-workgroup kernel
+    # keeps resident, so each row runs in one workgroup
+    d = rng.lognormal(0, 2, (8, 600001)).astype(np.float32)
+    t = rng.lognormal(0, 2, (8, 600001)).astype(np.float32)
+    t[:, 100000:100500] = 7.0
+    got = _sel_gpu(gpu_lib, d, t, 4, 256, 1000, 3000)
+    np.testing.assert_array_equal(got, vo.select_verify_set(d, t, 4, 256, 1000, 3000))
     say("case selector lognormal ragged")
     for L in (1, 31, 1025, 4099):
         d = rng.lognormal(0, 2, (2, L)).astype(np.float32)
