@@ -53,7 +53,8 @@ def algorithmic(cfg, n_ctx: int, sparse: bool):
 
 CSRC = os.path.join(ROOT, "long_context_verify_tree_amd", "csrc")
 KERNEL_SOURCES = {"partial_kernel": "va_attn.hip", "rows_kernel": "va_attn.hip", "select_kernel": "va_select.hip",
-                  "score_partial_kernel": "va_score.hip"}
+                  "select_cluster_kernel": "va_select.hip", "score_partial_kernel": "va_score.hip"}
+SELECT_SEG_TOKENS, SELECT_CLUSTER_TOKENS, SELECT_CLUSTER_MAX_GROUPS = 32768, 8192, 512
 
 
 def committed_traffic(kernel: str, workload: str):
@@ -82,6 +83,34 @@ def attention_kernel(cfg) -> str:
     """Which partial kernel the library picks: the shared-tile kernel for bf16
     with more than 64 query rows per KV head, the per-wavefront kernel else."""
     return "rows_kernel" if cfg.dtype == "bf16" and cfg.G * cfg.N > 64 else "partial_kernel"
+
+
+def select_kernel_name(B: int, L: int, budget: int) -> str:
+    """Which selector kernel the library runs: rows longer than one 32768-token
+    segment go to the multi-workgroup kernel when all its workgroups
+    (8192 tokens each) fit on the device at once."""
+    parts = -(-L // SELECT_CLUSTER_TOKENS)
+    if budget < L and L > SELECT_SEG_TOKENS and B * parts <= SELECT_CLUSTER_MAX_GROUPS:
+        return "select_cluster_kernel"
+    return "select_kernel"
+
+
+def verify_mode(cfg, verify: str) -> bool:
+    """True for a sparse step.  `auto` takes the workload's own mode (sparse
+    only when it has no dense run); `dense` / `sparse` pick one explicitly."""
+    if verify == "auto":
+        return cfg.sparse and not cfg.dense
+    if verify == "sparse" and not cfg.sparse:
+        raise SystemExit(f"{cfg.name} has no verify-set parameters")
+    return verify == "sparse"
+
+
+def workload_name(cfg, sparse: bool) -> str:
+    """The workload's name, with the verify mode appended when it is not the
+    workload's own (the 70B-shape sparse run, the Qwen-shape dense run)."""
+    if sparse == (cfg.sparse and not cfg.dense):
+        return cfg.name
+    return f"{cfg.name}_sparse{cfg.budget}" if sparse else f"{cfg.name}_dense"
 
 
 def measured_read_peak(torch, dev, gib: float = 2.0, reps: int = 10, min_seconds: float = 0.4):
@@ -123,13 +152,12 @@ def measured_read_peak(torch, dev, gib: float = 2.0, reps: int = 10, min_seconds
     return round(best, 1)
 
 
-def cpu_baseline(cfg, x, budget_s: float):
+def cpu_baseline(cfg, x, budget_s: float, sparse: bool):
     """The oracle, untouched, on as many (sequence, KV-head group) slabs of the
     benchmarked inputs as fit the time budget."""
     from threadpoolctl import threadpool_info
     from oracle import verify_oracle as vo
 
-    sparse = cfg.sparse and not cfg.dense
     t0 = time.perf_counter()
     idx = None
     if sparse:
@@ -152,7 +180,7 @@ def cpu_baseline(cfg, x, budget_s: float):
         "tokens_per_s_per_layer": round(cfg.B * cfg.N * frac / dt, 3),
         "cores": int(threads),
         "kind": "oracle",
-        "sample": f"{done}/{len(groups)} (sequence, KV head) slabs of the benchmarked {cfg.name} inputs"
+        "sample": f"{done}/{len(groups)} (sequence, KV head) slabs of the benchmarked {workload_name(cfg, sparse)} inputs"
                   f"{' incl. selection' if sparse else ''}, fp64 numpy, {dt:.1f} s",
         "host_cpus": os.cpu_count(),
     }
@@ -346,6 +374,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default=DEFAULT_CONFIG)
+    ap.add_argument("--verify", choices=("auto", "dense", "sparse"), default="auto",
+                    help="dense or sparse (verify-set) context; auto: the workload's own mode")
     ap.add_argument("--copies", type=int, default=0, help="input copies rotated over steps (0: auto)")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -373,8 +403,9 @@ def main():
     cfg = synth.CONFIGS[args.config]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    sparse = cfg.sparse and not cfg.dense
-    print(f"[bench] generating {cfg.name}", file=sys.stderr, flush=True)
+    sparse = verify_mode(cfg, args.verify)
+    wname = workload_name(cfg, sparse)
+    print(f"[bench] generating {wname}", file=sys.stderr, flush=True)
     x = synth.make_inputs(cfg, scores=cfg.sparse)
 
     def dv(a, dt):
@@ -460,7 +491,7 @@ def main():
     sel_avg = statistics.mean(sel_ms) if sparse else 0.0
     if sparse and sel_avg > part_avg:
         # the selector dominates: an HBM scan of both score rows plus the index write
-        kernel = "select_kernel"
+        kernel = select_kernel_name(cfg.B, cfg.L, cfg.budget)
         sel_bytes = 2 * cfg.B * cfg.L * 4 + cfg.B * n_ctx * 4
         ach = sel_bytes / (sel_avg * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -508,12 +539,18 @@ def main():
         "vs_baseline": None,
         "dtype": cfg.dtype,
         "data": f"synthetic (seeded N(0,1) q/K/V, {cfg.tree} tree; {copies} rotated input copies)",
-        "config": {"workload": cfg.name, "batch": cfg.B, "q_heads": cfg.Hq, "kv_heads": cfg.Hkv,
+        "config": {"workload": wname, "batch": cfg.B, "q_heads": cfg.Hq, "kv_heads": cfg.Hkv,
                    "head_dim": cfg.D, "context": cfg.L, "draft_nodes": cfg.N, "tree": cfg.tree,
                    "verify": "sparse" if sparse else "dense", "n_ctx_keys": n_ctx},
         "roofline": roof,
     }
-    roof["traffic"], roof["traffic_source"] = committed_traffic(kernel, cfg.name)
+    roof["traffic"], roof["traffic_source"] = committed_traffic(kernel, wname)
+    if sparse:
+        sel_bytes = 2 * cfg.B * cfg.L * 4 + cfg.B * n_ctx * 4
+        line["selector"] = {"kernel": select_kernel_name(cfg.B, cfg.L, cfg.budget), "us": round(sel_avg * 1e3, 2),
+                            "p10_p90_us": [round(pct(sel_ms, 10) * 1e3, 2), round(pct(sel_ms, 90) * 1e3, 2)],
+                            "bytes": sel_bytes, "gbs": round(sel_bytes / (sel_avg * 1e-3) / 1e9, 1),
+                            "share_of_step": round(sel_avg / ms_per_step, 4)}
     line["accept_commit"] = measure_commit(torch, ops, cfg, x, base, dev)
     line["importance_scores"] = measure_scores(torch, ops, cfg, base, dev, ms_per_step)
     line["draft_tree"] = measure_tree(torch, ops, cfg, dev)
@@ -527,7 +564,7 @@ def main():
         del src, dst
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle sample", file=sys.stderr, flush=True)
-        line["cpu_baseline"] = cpu_baseline(cfg, x, args.cpu_budget)
+        line["cpu_baseline"] = cpu_baseline(cfg, x, args.cpu_budget, sparse)
     else:
         line["cpu_baseline"] = None
     print(json.dumps(line), flush=True)

@@ -47,8 +47,9 @@
  *   last failing call on the calling thread.
  * - Device-side preconditions (parent, verify_idx contents) are not checked
  *   synchronously.  Violations stay memory-safe: a parent outside [-1, i) is
- *   treated as -1 and an index outside [0, L) is skipped, with an unspecified
- *   (but finite) result.
+ *   treated as -1; an index outside [0, L) reads no memory outside the cache
+ *   (it is skipped, or read as a zero key and value row); the result is then
+ *   unspecified (but finite).
  * - Workspace contents need no initialisation and are not preserved.
  *   Concurrent calls must use distinct workspaces.
  * - Calls keep no global mutable state and are thread-safe.

@@ -492,6 +492,9 @@ void partial_kernel(PartialParams p) {
     // dense context: every tile but the part's last is whole (no mask)
     k = ring_loop(nrot, std::false_type{});
   } else {
+    // tree and gathered parts run masked: a second (unmasked) variant of
+    // the compute step pushes the gathered shape, at two wavefronts per
+    // SIMD, past its 256 registers (it spilled and ran ~10% slower)
     k = ring_loop(nw, std::true_type{});
   }
   // the last (at most PF) tiles, already in their ring slots
@@ -690,10 +693,11 @@ void rows_kernel(PartialParams p) {
   u32x4 rg[RING][NCT];
   bool okr[RING];   // the thread's key exists (tile slot)
   int ixr[RING];    // gathered index of the thread's key in the tile the slot loads next
-  // Tile t of the part's walk.  Context tiles (all but a partial last one)
-  // start at a per-head offset, so heads do not read the same DRAM channels
-  // in step; past the end a slot re-fetches the last tile, never staged.
-  const int nrot = tree ? 0 : (gather ? ntiles : (ke - kb) / kTileKeys);
+  // Tile t of the part's walk.  Whole context tiles (all but a partial last
+  // one) start at a per-head offset, so heads do not read the same DRAM
+  // channels in step; the partial tile comes last; past the end a slot
+  // re-fetches the last tile, never staged.
+  const int nrot = tree ? 0 : (ke - kb) / kTileKeys;
   const int rot = VA_ROTATE && nrot > 0 ? (int)((int64_t)(b * p.Hkv + kvh) * nrot / ((int64_t)p.B * p.Hkv)) : 0;
   auto clamp_tile = [&](int t) __attribute__((always_inline)) -> int {
     if (t < nrot) {
@@ -865,11 +869,14 @@ void rows_kernel(PartialParams p) {
       }
     }
   };
-  if (tree || gather) {
+  if (tree) {
     tile_loop(ntiles, std::true_type{});
   } else {
-    // whole tiles without the mask, then the partial tail tile (staged in
-    // buffer nfull % NSTAGE, its S in s_cur) with it
+    // whole context tiles (dense or gathered) without the mask, then the
+    // partial tail tile (staged in buffer nfull % NSTAGE, its S in s_cur)
+    // with it.  A gathered index outside [0, L) in a whole tile reads as a
+    // zero key and value row (a precondition violation: memory-safe, result
+    // unspecified but finite).
     const int nfull = (ke - kb) / kTileKeys;
     tile_loop(nfull, std::false_type{});
     if (nfull < ntiles) soft_pv(s_cur, nfull, nfull % NSTAGE, std::true_type{});
