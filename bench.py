@@ -152,6 +152,48 @@ def measured_read_peak(torch, dev, gib: float = 2.0, reps: int = 10, min_seconds
     return round(best, 1)
 
 
+def measured_gather_peak(torch, sets, idx_bufs, cfg, n_ctx: int, reps: int = 8):
+    """Achievable rate (GB/s) of the sparse step's gathered K/V reads: the
+    probe library reads the same rows (each input copy with the index list
+    selected for it, copies rotated as in the timed steps) with no compute."""
+    import ctypes
+    path = os.path.join(ROOT, "long_context_verify_tree_amd", "libva_probe.so")
+    if not os.path.exists(path) or n_ctx <= 0:
+        return None
+    lib = ctypes.CDLL(path)
+    fn = lib.va_probe_gather_read
+    fn.restype = ctypes.c_int
+    fn.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p] + [ctypes.c_int] * 5 + [ctypes.c_void_p,
+                                                                                             ctypes.c_int,
+                                                                                             ctypes.c_void_p]
+    e = 4 if cfg.dtype == "fp32" else 2
+    row_bytes = cfg.D * e
+    for st in sets:   # the probe takes [B, Hkv, L, D] rows back to back
+        assert st["k_cache"].is_contiguous() and st["v_cache"].is_contiguous()
+    for ib in idx_bufs:
+        assert ib.is_contiguous() and ib.shape == (cfg.B, n_ctx)
+    sink = torch.zeros(1, dtype=torch.int32, device=sets[0]["k_cache"].device)
+    stream = torch.cuda.current_stream().cuda_stream
+    nbytes = 2 * cfg.B * cfg.Hkv * n_ctx * row_bytes
+    best = 0.0
+    for grid in (256 * 8, 256 * 16, 256 * 32):
+        def run(i):
+            st = sets[i % len(sets)]
+            rc = fn(st["k_cache"].data_ptr(), st["v_cache"].data_ptr(), idx_bufs[i % len(sets)].data_ptr(), cfg.B,
+                    cfg.Hkv, n_ctx, cfg.L, row_bytes, sink.data_ptr(), grid, stream)
+            if rc != 0:
+                raise RuntimeError(f"va_probe_gather_read failed: {rc}")
+        run(0)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for i in range(reps):
+            run(i + 1)
+        b.record()
+        b.synchronize()
+        best = max(best, reps * nbytes / (a.elapsed_time(b) * 1e-3) / 1e9)
+    return round(best, 1)
+
+
 def cpu_baseline(cfg, x, budget_s: float, sparse: bool):
     """The oracle, untouched, on as many (sequence, KV-head group) slabs of the
     benchmarked inputs as fit the time budget."""
@@ -546,6 +588,16 @@ def main():
     }
     roof["traffic"], roof["traffic_source"] = committed_traffic(kernel, wname)
     if sparse:
+        # gathered reads alone, on the same rows: the ceiling of the sparse attention kernel's HBM rate
+        for i, st in enumerate(sets):   # every copy's index list, as its steps select it
+            ops.select_verify_set(st["draft_score"], st["target_score"], sink=cfg.sink, window=cfg.window,
+                                  top_m=cfg.top_m, budget=cfg.budget, out=idx_bufs[i], workspace=sel_ws)
+        torch.cuda.synchronize()
+        gpeak = measured_gather_peak(torch, sets, idx_bufs, cfg, n_ctx)
+        att_gbs = a["partial_bytes"] / (part_avg * 1e-3) / 1e9
+        line["gather_probe"] = {"gbs": gpeak, "bytes_per_call": 2 * cfg.B * cfg.Hkv * n_ctx * cfg.D * es,
+                                "attention_kernel": attention_kernel(cfg), "attention_kernel_gbs": round(att_gbs, 1),
+                                "attention_frac_of_gather_probe": round(att_gbs / gpeak, 4) if gpeak else None}
         sel_bytes = 2 * cfg.B * cfg.L * 4 + cfg.B * n_ctx * 4
         line["selector"] = {"kernel": select_kernel_name(cfg.B, cfg.L, cfg.budget), "us": round(sel_avg * 1e3, 2),
                             "p10_p90_us": [round(pct(sel_ms, 10) * 1e3, 2), round(pct(sel_ms, 90) * 1e3, 2)],
