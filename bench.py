@@ -57,11 +57,12 @@ KERNEL_SOURCES = {"partial_kernel": "va_attn.hip", "rows_kernel": "va_attn.hip",
 SELECT_SEG_TOKENS, SELECT_CLUSTER_TOKENS, SELECT_CLUSTER_MAX_GROUPS = 32768, 8192, 512
 
 
-def committed_traffic(kernel: str, workload: str):
-    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
-    summary, or None if there is none or the kernel source changed since."""
+def committed_summary(kernel: str, workload: str, suffix: str = ""):
+    """Fields of the committed rocprofv3 summary profiles/<kernel>_<workload><suffix>.md
+    as (fields, path), or (None, note) if there is none or the kernel source
+    changed since it was taken."""
     import hashlib
-    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}.md")
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}{suffix}.md")
     if not os.path.exists(path):
         return None, None
     fields = {}
@@ -73,10 +74,27 @@ def committed_traffic(kernel: str, workload: str):
     h = hashlib.sha256()
     for name in (KERNEL_SOURCES[kernel], "va_device.h"):
         h.update(open(os.path.join(CSRC, name), "rb").read())
-    digest = h.hexdigest()
-    if fields.get("kernel source sha256") != digest or "traffic bytes per launch" not in fields:
+    if fields.get("kernel source sha256") != h.hexdigest():
         return None, os.path.relpath(path, ROOT) + " (stale: kernel changed since the counters were taken)"
-    return int(float(fields["traffic bytes per launch"])), os.path.relpath(path, ROOT)
+    return fields, os.path.relpath(path, ROOT)
+
+
+def committed_traffic(kernel: str, workload: str):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    summary, or None if there is none or the kernel source changed since."""
+    fields, src = committed_summary(kernel, workload)
+    if fields is None or "traffic bytes per launch" not in fields:
+        return None, src
+    return int(float(fields["traffic bytes per launch"])), src
+
+
+def committed_mfma_util(kernel: str, workload: str):
+    """MFMA-busy percentage (rocprofv3's MfmaUtil) of `kernel` from the
+    committed pipe-counter summary, or None (missing or stale)."""
+    fields, src = committed_summary(kernel, workload, "_pipes")
+    if fields is None or "mfma util percent" not in fields:
+        return None, src
+    return float(fields["mfma util percent"]), src
 
 
 def attention_kernel(cfg) -> str:
@@ -587,6 +605,10 @@ def main():
         "roofline": roof,
     }
     roof["traffic"], roof["traffic_source"] = committed_traffic(kernel, wname)
+    # cross-check of the MFMA share: the MFMA pipe's busy fraction from rocprofv3 counters, where taken
+    mfma_pct, mfma_src = committed_mfma_util(kernel, wname)
+    if mfma_src is not None:
+        roof["mfma_busy_counter_pct"], roof["mfma_counter_source"] = mfma_pct, mfma_src
     if sparse:
         # gathered reads alone, on the same rows: the ceiling of the sparse attention kernel's HBM rate
         for i, st in enumerate(sets):   # every copy's index list, as its steps select it
