@@ -243,7 +243,19 @@ def cpu_baseline(cfg, x, budget_s: float, sparse: bool):
         "sample": f"{done}/{len(groups)} (sequence, KV head) slabs of the benchmarked {workload_name(cfg, sparse)} inputs"
                   f"{' incl. selection' if sparse else ''}, fp64 numpy, {dt:.1f} s",
         "host_cpus": os.cpu_count(),
+        "cpu_model": cpu_model(),
     }
+
+
+def cpu_model() -> str:
+    """The host CPU's model name (Linux /proc/cpuinfo), or "unknown"."""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def measure_commit(torch, ops, cfg, x, base, dev, reps: int = 20):
