@@ -73,3 +73,10 @@ def test_committed_summaries_fresh_and_stale(tmp_path, monkeypatch):
 
 def test_cpu_model_is_a_string():
     assert isinstance(bench.cpu_model(), str) and bench.cpu_model()
+
+
+def test_more_than_one_gpu_is_refused():
+    import subprocess
+    res = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                         text=True, timeout=120)
+    assert res.returncode == 2 and "one GPU only" in res.stderr
