@@ -54,7 +54,7 @@ def algorithmic(cfg, n_ctx: int, sparse: bool):
 CSRC = os.path.join(ROOT, "long_context_verify_tree_amd", "csrc")
 KERNEL_SOURCES = {"partial_kernel": "va_attn.hip", "rows_kernel": "va_attn.hip", "select_kernel": "va_select.hip",
                   "select_cluster_kernel": "va_select.hip", "score_partial_kernel": "va_score.hip"}
-SELECT_SEG_TOKENS, SELECT_CLUSTER_TOKENS, SELECT_CLUSTER_MAX_GROUPS = 32768, 8192, 512
+SELECT_SEG_TOKENS, SELECT_CLUSTER_TOKENS, SELECT_CLUSTER_MAX_GROUPS = 32768, 16384, 256
 
 
 def committed_summary(kernel: str, workload: str, suffix: str = ""):
@@ -106,7 +106,7 @@ def attention_kernel(cfg) -> str:
 def select_kernel_name(B: int, L: int, budget: int) -> str:
     """Which selector kernel the library runs: rows longer than one 32768-token
     segment go to the multi-workgroup kernel when all its workgroups
-    (8192 tokens each) fit on the device at once."""
+    (16384 tokens each) fit on the device at once."""
     parts = -(-L // SELECT_CLUSTER_TOKENS)
     if budget < L and L > SELECT_SEG_TOKENS and B * parts <= SELECT_CLUSTER_MAX_GROUPS:
         return "select_cluster_kernel"

@@ -24,7 +24,7 @@
 // registers for all passes; longer rows re-read each segment per pass (the
 // row then sits in L2).  Rows longer than one segment go to a second kernel
 // instead (select_cluster_kernel, below) when the batch is small enough:
-// several workgroups per row, each holding 8192 tokens in registers.
+// several workgroups per row, each holding 16384 tokens in registers.
 
 #include <stdint.h>
 
@@ -319,10 +319,13 @@ __global__ __launch_bounds__(kST) void select_kernel(SelParams p) {
 // the launch is used only when all B * P workgroups fit on the device at
 // once, which the waits rely on.
 
-constexpr int kCT = 256;                   // threads per workgroup
+#ifndef VA_SEL_CT
+#define VA_SEL_CT 512   // 128: 83 us, 256: 64 us, 512: 58 us, 1024: 69 us on 4 rows of 131072
+#endif
+constexpr int kCT = VA_SEL_CT;             // threads per workgroup
 constexpr int kCWaves = kCT / 64;
-constexpr int kCSeg = kCT * kKPT;          // 8192 tokens per workgroup
-constexpr int kCMaxGroups = 512;           // B * P limit: every workgroup resident
+constexpr int kCSeg = kCT * kKPT;          // 16384 tokens per workgroup
+constexpr int kCMaxGroups = 256;           // B * P limit: every workgroup resident (one per CU; two fit)
 constexpr int kSpinLimit = 1 << 18;        // polls per wait (each a device-coherent load: < 1 s)
 
 // Workspace of one row, in ints, zeroed before the launch.
@@ -554,7 +557,8 @@ __global__ __launch_bounds__(256) void zero_ints_kernel(int* p, int64_t n) {
 // one-segment row in registers, while longer rows are re-read on every pass;
 // a row barrier costs a few microseconds), and every workgroup resident at
 // once.  Measured: 16 rows of 32768 tokens 36 us in select_kernel, 53 us
-// here; 4 rows of 131072 tokens 178 us there, 58 us here.
+// here (256-thread workgroups); 4 rows of 131072 tokens 178 us there, 58 us
+// here (64 us with 256-thread workgroups).
 inline int cluster_parts(int32_t B, int32_t L) {
   const int P = (int)(((int64_t)L + kCSeg - 1) / kCSeg);
   return L > kSeg && (int64_t)B * P <= kCMaxGroups ? P : 0;

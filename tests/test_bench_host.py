@@ -35,8 +35,8 @@ def test_selector_kernel_choice():
     assert bench.select_kernel_name(16, 32768, 2048) == "select_kernel"
     # longer rows whose 8192-token workgroups all fit at once: several workgroups per row
     assert bench.select_kernel_name(4, 131072, 4096) == "select_cluster_kernel"
-    assert bench.select_kernel_name(32, 131072, 4096) == "select_cluster_kernel"    # 32 * 16 = 512 groups
-    assert bench.select_kernel_name(33, 131072, 4096) == "select_kernel"            # 528 > 512
+    assert bench.select_kernel_name(32, 131072, 4096) == "select_cluster_kernel"    # 32 * 8 = 256 groups
+    assert bench.select_kernel_name(33, 131072, 4096) == "select_kernel"            # 264 > 256
     # budget >= L: every index, no selection kernel of the cluster kind
     assert bench.select_kernel_name(4, 131072, 131072) == "select_kernel"
 
