@@ -59,15 +59,24 @@ __device__ inline uint32_t order_key(float f) {
 // Exclusive prefix sum of v over the workgroup in thread order; *total gets
 // the sum.  Uses wsum[kSWaves]; two barriers, or one with TAIL = false when
 // the caller reaches another barrier before wsum is written again.
+// Inclusive prefix sum over the 64 lanes of a wavefront with DPP moves (no
+// LDS round trip): shifts by 1, 2, 4, 8 within each row of 16 lanes (lanes
+// without a source read 0), then lane 15 of rows 0 and 2 is added to rows 1
+// and 3, and lane 31 to rows 2 and 3.
+__device__ inline int wave_incl_scan(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, true);   // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, true);   // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, true);   // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, true);   // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15 into rows 1, 3
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31 into rows 2, 3
+  return x;
+}
+
 template <bool TAIL = true, int NW = kSWaves>
 __device__ inline int block_excl_scan(int v, int* wsum, int* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int x = v;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int y = __shfl_up(x, off);
-    if (lane >= off) x += y;
-  }
+  const int x = wave_incl_scan(v);
   if (lane == 63) wsum[wave] = x;
   __syncthreads();
   int before = 0, tot = 0;
