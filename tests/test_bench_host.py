@@ -80,3 +80,11 @@ def test_more_than_one_gpu_is_refused():
     res = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
                          text=True, timeout=120)
     assert res.returncode == 2 and "one GPU only" in res.stderr
+
+
+def test_committed_mfma_util():
+    pct, src = bench.committed_mfma_util("rows_kernel", "l70b_tree128_L128k")
+    assert src == "profiles/rows_kernel_l70b_tree128_L128k_pipes.md"
+    assert pct is not None and 0.0 < pct < 100.0
+    # no pipe summary for this kernel and workload
+    assert bench.committed_mfma_util("select_kernel", "qwen25_7b_sparse2048_L32k") == (None, None)
