@@ -33,7 +33,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0 # dense bf16
 MFMA_FP32_PEAK_TFLOPS = 157.3
-DEFAULT_CONFIG = "llama3_8b_chain8_L32k"
+DEFAULT_CONFIG = "l70b_tree128_L128k"
 
 
 def algorithmic(cfg, n_ctx: int, sparse: bool):
@@ -294,32 +294,35 @@ def measure_commit(torch, ops, cfg, x, base, dev, reps: int = 20):
 SCORE_HEADS = 2   # scoring heads of the importance map (a few selected heads)
 
 
-def measure_scores(torch, ops, cfg, base, dev, step_ms, reps: int = 20):
+def measure_scores(torch, ops, cfg, sets, dev, step_ms, reps: int = 20):
     """Importance map of SCORE_HEADS scoring heads with (up to 32 of) the
     draft rows each, over the benchmarked cache's first KV heads; mean of
-    `reps` calls timed with HIP events on the launching stream."""
+    `reps` calls timed with HIP events on the launching stream.  The calls
+    rotate over the input copies as the verification steps do, so the
+    scoring heads' K rows come from HBM, not from the 256 MB MALL."""
     if cfg.dtype != "bf16" or cfg.L == 0:
         return None
     hs = min(SCORE_HEADS, cfg.Hkv)
     rows = min(cfg.N, 32)                      # scoring rows per head (the kernel takes up to 32)
-    q = base["q"][:, :hs, :rows]
-    k = base["k_cache"][:, :hs]
-    desc = ops.make_score_desc(q, k)
+    qs = [st["q"][:, :hs, :rows] for st in sets]
+    ks = [st["k_cache"][:, :hs] for st in sets]
+    desc = ops.make_score_desc(qs[0], ks[0])
     ws = torch.empty(ops.scores_workspace_size(desc), dtype=torch.uint8, device=dev)
     out = torch.empty(cfg.B, cfg.L, dtype=torch.float32, device=dev)
-    ops.importance_scores(q, k, out=out, workspace=ws, desc=desc)
+    ops.importance_scores(qs[0], ks[0], out=out, workspace=ws, desc=desc)
     torch.cuda.synchronize()
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     a.record()
-    for _ in range(reps):
-        ops.importance_scores(q, k, out=out, workspace=ws, desc=desc)
+    for i in range(reps):
+        j = (i + 1) % len(sets)
+        ops.importance_scores(qs[j], ks[j], out=out, workspace=ws, desc=desc)
     b.record()
     b.synchronize()
     us = a.elapsed_time(b) * 1e3 / reps
     nbytes = cfg.B * hs * (cfg.L + rows) * cfg.D * 2 + cfg.B * cfg.L * 4   # K and q read, map written
     return {"us": round(us, 2), "bytes": nbytes, "gbs": round(nbytes / (us * 1e-6) / 1e9, 1),
             "frac_of_hbm_peak": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
-            "scoring_heads": hs, "rows_per_head": rows,
+            "scoring_heads": hs, "rows_per_head": rows, "input_copies_rotated": len(sets),
             "vs_one_verification_step": round(us * 1e-3 / step_ms, 4),
             "kernels": ["score_partial_kernel", "score_finish_kernel"]}
 
@@ -440,67 +443,13 @@ def sweep_n(args):
     print(json.dumps(line), flush=True)
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", default=DEFAULT_CONFIG)
-    ap.add_argument("--verify", choices=("auto", "dense", "sparse"), default="auto",
-                    help="dense or sparse (verify-set) context; auto: the workload's own mode")
-    ap.add_argument("--copies", type=int, default=0, help="input copies rotated over steps (0: auto)")
-    ap.add_argument("--cpu-budget", type=float, default=15.0)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--sweep-n", action="store_true",
-                    help="instead of the step benchmark: time verification for N = 1..256 draft nodes on the "
-                         "workload's cache, calibrate the roofline time model and run the tree-size controller")
-    ap.add_argument("--no-read-probe", action="store_true",
-                    help="skip the read-only HBM probe (counter-collection runs)")
-    ap.add_argument("--copy-calib-gib", type=float, default=0.0,
-                    help="after timing, run a plain device copy of this many GiB (HBM counter calibration)")
-    args = ap.parse_args()
-
-    if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for {args.gpus}); the kernels use no collectives",
-              file=sys.stderr)
-        sys.exit(2)
-    if args.sweep_n:
-        sweep_n(args)
-        return
-
-    import torch
-    from long_context_verify_tree_amd import ops, synth
-
-    ops.load()
-    cfg = synth.CONFIGS[args.config]
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    sparse = verify_mode(cfg, args.verify)
-    wname = workload_name(cfg, sparse)
-    print(f"[bench] generating {wname}", file=sys.stderr, flush=True)
-    x = synth.make_inputs(cfg, scores=cfg.sparse)
-
-    def dv(a, dt):
-        if dt == synth.BF16:
-            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
-        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
-
-    base = dict(q=dv(x.q, cfg.dtype), k_cache=dv(x.k_cache, cfg.dtype), v_cache=dv(x.v_cache, cfg.dtype),
-                k_draft=dv(x.k_draft, cfg.dtype), v_draft=dv(x.v_draft, cfg.dtype),
-                parent=torch.from_numpy(x.parent).to(dev))
-    if sparse:
-        base["draft_score"] = dv(x.draft_score, synth.FP32)
-        base["target_score"] = dv(x.target_score, synth.FP32)
-    # Bytes one step reads from its input copy (gathered rows and scores when
-    # sparse).  At least four copies rotate, and enough that a copy is read
-    # again only after more than twice the 256 MB MALL of other inputs.
-    es = 4 if cfg.dtype == "fp32" else 2
-    n_keys = min(cfg.budget, cfg.L) if sparse else cfg.L
-    step_read = 2 * cfg.B * cfg.Hkv * n_keys * cfg.D * es + (2 * cfg.B * cfg.L * 4 if sparse else 0)
-    copies = args.copies or int(min(16, max(4, 1 + np.ceil(512e6 / max(step_read, 1)))))
-    sets = [base] + [{k: v.clone() for k, v in base.items()} for _ in range(copies - 1)]
-
+def run_steps(torch, ops, cfg, sparse: bool, sets, dev, steps: int, warmup: int):
+    """Times `steps` whole verification steps (selector when sparse, partials,
+    merge) of one mode over the rotated input copies, after `warmup` untimed
+    ones; then the same steps again with HIP events on the launching stream
+    around each stage.  Returns the timings and the buffers of the last step."""
     n_ctx = min(cfg.budget, cfg.L) if sparse else cfg.L
+    base = sets[0]
     out = torch.empty_like(base["q"])
     lse = torch.empty(cfg.B, cfg.Hq, cfg.N, dtype=torch.float32, device=dev)
     desc = ops.make_desc(base["q"], base["k_cache"], base["v_cache"], base["k_draft"], base["v_draft"], out)
@@ -528,39 +477,38 @@ def main():
         if ev is not None:
             ev[3].record()
 
-    # achievable read bandwidth; this also brings the clock up before warm-up
-    read_peak = None if args.no_read_probe else measured_read_peak(torch, dev)
-    for i in range(args.warmup):
+    for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
-    # timed region: exactly K whole steps, nothing else on the stream
+    # timed region: exactly `steps` whole steps, nothing else on the stream
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(args.warmup + i)
+    for i in range(steps):
+        step(warmup + i)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    # the same K steps again with HIP events on the launching stream around
-    # each stage, for the per-kernel durations the roofline uses
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    for i in range(args.steps):
-        step(args.warmup + args.steps + i, evs[i])
+    for i in range(steps):
+        step(warmup + steps + i, evs[i])
     torch.cuda.synchronize()
     wall_ev = time.perf_counter() - t1
+    return dict(n_ctx=n_ctx, ms_per_step=wall * 1e3 / steps, wall_ev=wall_ev,
+                sel_ms=[e[0].elapsed_time(e[1]) for e in evs], part_ms=[e[1].elapsed_time(e[2]) for e in evs],
+                merge_ms=[e[2].elapsed_time(e[3]) for e in evs], idx_bufs=idx_bufs, sel_ws=sel_ws)
 
-    sel_ms = [e[0].elapsed_time(e[1]) for e in evs]
-    part_ms = [e[1].elapsed_time(e[2]) for e in evs]
-    merge_ms = [e[2].elapsed_time(e[3]) for e in evs]
-    ms_per_step = wall * 1e3 / args.steps
+
+def _pct(xs, q):
+    return round(float(np.percentile(xs, q)), 4)
+
+
+def roofline_of(cfg, sparse: bool, r, read_peak, wname):
+    """The roofline object of the dominant kernel of one mode's steps: the
+    partial (or rows) kernel, or the selector when it is slower."""
+    n_ctx = r["n_ctx"]
     a = algorithmic(cfg, n_ctx, sparse)
-    value = a["step_bytes"] / (ms_per_step * 1e-3) / 1e9
-
-    def pct(xs, q):
-        return round(float(np.percentile(xs, q)), 4)
-
-    part_avg = statistics.mean(part_ms)
-    sel_avg = statistics.mean(sel_ms) if sparse else 0.0
+    part_avg = statistics.mean(r["part_ms"])
+    sel_avg = statistics.mean(r["sel_ms"]) if sparse else 0.0
     if sparse and sel_avg > part_avg:
         # the selector dominates: an HBM scan of both score rows plus the index write
         kernel = select_kernel_name(cfg.B, cfg.L, cfg.budget)
@@ -582,7 +530,7 @@ def main():
             roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None}
         roof["kernel_avg_us"] = round(part_avg * 1e3, 2)
-        roof["kernel_p10_p90_us"] = [round(pct(part_ms, 10) * 1e3, 2), round(pct(part_ms, 90) * 1e3, 2)]
+        roof["kernel_p10_p90_us"] = [round(_pct(r["part_ms"], 10) * 1e3, 2), round(_pct(r["part_ms"], 90) * 1e3, 2)]
         roof["algorithmic_bytes_per_launch"] = a["partial_bytes"]
         roof["algorithmic_flops_per_launch"] = a["flops"]
         roof["hbm_gbs"] = round(achieved, 1)
@@ -590,6 +538,124 @@ def main():
             roof["frac_of_measured_read_peak"] = round(achieved / read_peak, 4)
     roof["kernel"] = kernel
     roof["measured_read_peak_gbs"] = read_peak
+    roof["traffic"], roof["traffic_source"] = committed_traffic(kernel, wname)
+    # cross-check of the MFMA share: the MFMA pipe's busy fraction from rocprofv3 counters, where taken
+    mfma_pct, mfma_src = committed_mfma_util(kernel, wname)
+    if mfma_src is not None:
+        roof["mfma_busy_counter_pct"], roof["mfma_counter_source"] = mfma_pct, mfma_src
+    return roof
+
+
+def sparse_extras(torch, ops, cfg, sets, r, es):
+    """Selector figures and the gathered-read ceiling of a sparse mode."""
+    n_ctx = r["n_ctx"]
+    idx_bufs = r["idx_bufs"]
+    for i, st in enumerate(sets):   # every copy's index list, as its steps select it
+        ops.select_verify_set(st["draft_score"], st["target_score"], sink=cfg.sink, window=cfg.window,
+                              top_m=cfg.top_m, budget=cfg.budget, out=idx_bufs[i], workspace=r["sel_ws"])
+    torch.cuda.synchronize()
+    gpeak = measured_gather_peak(torch, sets, idx_bufs, cfg, n_ctx)
+    a = algorithmic(cfg, n_ctx, True)
+    part_avg = statistics.mean(r["part_ms"])
+    sel_avg = statistics.mean(r["sel_ms"])
+    att_gbs = a["partial_bytes"] / (part_avg * 1e-3) / 1e9
+    gather = {"gbs": gpeak, "bytes_per_call": 2 * cfg.B * cfg.Hkv * n_ctx * cfg.D * es,
+              "attention_kernel": attention_kernel(cfg), "attention_kernel_gbs": round(att_gbs, 1),
+              "attention_frac_of_gather_probe": round(att_gbs / gpeak, 4) if gpeak else None}
+    sel_bytes = 2 * cfg.B * cfg.L * 4 + cfg.B * n_ctx * 4
+    selector = {"kernel": select_kernel_name(cfg.B, cfg.L, cfg.budget), "us": round(sel_avg * 1e3, 2),
+                "p10_p90_us": [round(_pct(r["sel_ms"], 10) * 1e3, 2), round(_pct(r["sel_ms"], 90) * 1e3, 2)],
+                "bytes": sel_bytes, "gbs": round(sel_bytes / (sel_avg * 1e-3) / 1e9, 1),
+                "share_of_step": round(sel_avg / r["ms_per_step"], 4)}
+    return gather, selector
+
+
+def stage_summary(r, sparse):
+    return {"select": round(statistics.median(r["sel_ms"]), 4) if sparse else 0.0,
+            "partials": round(statistics.median(r["part_ms"]), 4),
+            "merge": round(statistics.median(r["merge_ms"]), 4),
+            "partials_p10_p90": [_pct(r["part_ms"], 10), _pct(r["part_ms"], 90)],
+            "instrumented_step": round(r["wall_ev"] * 1e3 / len(r["part_ms"]), 4)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default=DEFAULT_CONFIG)
+    ap.add_argument("--verify", choices=("auto", "dense", "sparse"), default="auto",
+                    help="dense or sparse (verify-set) context; auto: the workload's own mode")
+    ap.add_argument("--copies", type=int, default=0, help="input copies rotated over steps (0: auto)")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-other-mode", action="store_true",
+                    help="skip the second verify mode of a workload that has both (dense and sparse)")
+    ap.add_argument("--sweep-n", action="store_true",
+                    help="instead of the step benchmark: time verification for N = 1..256 draft nodes on the "
+                         "workload's cache, calibrate the roofline time model and run the tree-size controller")
+    ap.add_argument("--no-read-probe", action="store_true",
+                    help="skip the read-only HBM probe (counter-collection runs)")
+    ap.add_argument("--copy-calib-gib", type=float, default=0.0,
+                    help="after timing, run a plain device copy of this many GiB (HBM counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}); the kernels use no collectives",
+              file=sys.stderr)
+        sys.exit(2)
+    if args.sweep_n:
+        sweep_n(args)
+        return
+
+    import torch
+    from long_context_verify_tree_amd import ops, synth
+
+    ops.load()
+    cfg = synth.CONFIGS[args.config]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    sparse = verify_mode(cfg, args.verify)
+    wname = workload_name(cfg, sparse)
+    # the workload's other verify mode (the 70B-shape sparse run beside its dense headline)
+    other = None
+    if args.verify == "auto" and cfg.sparse and cfg.dense and not args.no_other_mode:
+        other = not sparse
+    need_scores = sparse or other is True
+    print(f"[bench] generating {wname}", file=sys.stderr, flush=True)
+    x = synth.make_inputs(cfg, scores=need_scores)
+
+    def dv(a, dt):
+        if dt == synth.BF16:
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    base = dict(q=dv(x.q, cfg.dtype), k_cache=dv(x.k_cache, cfg.dtype), v_cache=dv(x.v_cache, cfg.dtype),
+                k_draft=dv(x.k_draft, cfg.dtype), v_draft=dv(x.v_draft, cfg.dtype),
+                parent=torch.from_numpy(x.parent).to(dev))
+    if need_scores:
+        base["draft_score"] = dv(x.draft_score, synth.FP32)
+        base["target_score"] = dv(x.target_score, synth.FP32)
+    # Bytes one step reads from its input copy (gathered rows and scores when
+    # sparse).  At least four copies rotate, and enough that a copy is read
+    # again only after more than twice the 256 MB MALL of other inputs.
+    es = 4 if cfg.dtype == "fp32" else 2
+
+    def copies_for(sp):
+        n_keys = min(cfg.budget, cfg.L) if sp else cfg.L
+        step_read = 2 * cfg.B * cfg.Hkv * n_keys * cfg.D * es + (2 * cfg.B * cfg.L * 4 if sp else 0)
+        return int(min(16, max(4, 1 + np.ceil(512e6 / max(step_read, 1)))))
+    copies = args.copies or max(copies_for(sparse), copies_for(other) if other is not None else 0)
+    sets = [base] + [{k: v.clone() for k, v in base.items()} for _ in range(copies - 1)]
+
+    # achievable read bandwidth; this also brings the clock up before warm-up
+    read_peak = None if args.no_read_probe else measured_read_peak(torch, dev)
+    r = run_steps(torch, ops, cfg, sparse, sets, dev, args.steps, args.warmup)
+    n_ctx = r["n_ctx"]
+    ms_per_step = r["ms_per_step"]
+    a = algorithmic(cfg, n_ctx, sparse)
+    value = a["step_bytes"] / (ms_per_step * 1e-3) / 1e9
+    roof = roofline_of(cfg, sparse, r, read_peak, wname)
 
     line = {
         "metric": "verify-attention HBM GB/s (% of peak) + draft tokens verified/sec per layer",
@@ -601,11 +667,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 4),
-        "stage_ms": {"select": round(statistics.median(sel_ms), 4) if sparse else 0.0,
-                     "partials": round(statistics.median(part_ms), 4),
-                     "merge": round(statistics.median(merge_ms), 4),
-                     "partials_p10_p90": [pct(part_ms, 10), pct(part_ms, 90)],
-                     "instrumented_step": round(wall_ev * 1e3 / args.steps, 4)},
+        "stage_ms": stage_summary(r, sparse),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -616,29 +678,27 @@ def main():
                    "verify": "sparse" if sparse else "dense", "n_ctx_keys": n_ctx},
         "roofline": roof,
     }
-    roof["traffic"], roof["traffic_source"] = committed_traffic(kernel, wname)
-    # cross-check of the MFMA share: the MFMA pipe's busy fraction from rocprofv3 counters, where taken
-    mfma_pct, mfma_src = committed_mfma_util(kernel, wname)
-    if mfma_src is not None:
-        roof["mfma_busy_counter_pct"], roof["mfma_counter_source"] = mfma_pct, mfma_src
     if sparse:
-        # gathered reads alone, on the same rows: the ceiling of the sparse attention kernel's HBM rate
-        for i, st in enumerate(sets):   # every copy's index list, as its steps select it
-            ops.select_verify_set(st["draft_score"], st["target_score"], sink=cfg.sink, window=cfg.window,
-                                  top_m=cfg.top_m, budget=cfg.budget, out=idx_bufs[i], workspace=sel_ws)
-        torch.cuda.synchronize()
-        gpeak = measured_gather_peak(torch, sets, idx_bufs, cfg, n_ctx)
-        att_gbs = a["partial_bytes"] / (part_avg * 1e-3) / 1e9
-        line["gather_probe"] = {"gbs": gpeak, "bytes_per_call": 2 * cfg.B * cfg.Hkv * n_ctx * cfg.D * es,
-                                "attention_kernel": attention_kernel(cfg), "attention_kernel_gbs": round(att_gbs, 1),
-                                "attention_frac_of_gather_probe": round(att_gbs / gpeak, 4) if gpeak else None}
-        sel_bytes = 2 * cfg.B * cfg.L * 4 + cfg.B * n_ctx * 4
-        line["selector"] = {"kernel": select_kernel_name(cfg.B, cfg.L, cfg.budget), "us": round(sel_avg * 1e3, 2),
-                            "p10_p90_us": [round(pct(sel_ms, 10) * 1e3, 2), round(pct(sel_ms, 90) * 1e3, 2)],
-                            "bytes": sel_bytes, "gbs": round(sel_bytes / (sel_avg * 1e-3) / 1e9, 1),
-                            "share_of_step": round(sel_avg / ms_per_step, 4)}
+        line["gather_probe"], line["selector"] = sparse_extras(torch, ops, cfg, sets, r, es)
+    if other is not None:
+        # the same inputs verified in the workload's other mode, timed the same way
+        print(f"[bench] timing the {'sparse' if other else 'dense'} mode", file=sys.stderr, flush=True)
+        oname = workload_name(cfg, other)
+        r2 = run_steps(torch, ops, cfg, other, sets, dev, args.steps, args.warmup)
+        a2 = algorithmic(cfg, r2["n_ctx"], other)
+        o = {"workload": oname, "verify": "sparse" if other else "dense", "n_ctx_keys": r2["n_ctx"],
+             "ms_per_step": round(r2["ms_per_step"], 4),
+             "gbs": round(a2["step_bytes"] / (r2["ms_per_step"] * 1e-3) / 1e9, 1),
+             "draft_tokens_verified_per_s_per_layer": round(cfg.B * cfg.N / (r2["ms_per_step"] * 1e-3), 1),
+             "speedup_vs_" + ("dense" if other else "sparse"):
+                 round((ms_per_step / r2["ms_per_step"]) if other else (r2["ms_per_step"] / ms_per_step), 3),
+             "stage_ms": stage_summary(r2, other),
+             "roofline": roofline_of(cfg, other, r2, read_peak, oname)}
+        if other:
+            o["gather_probe"], o["selector"] = sparse_extras(torch, ops, cfg, sets, r2, es)
+        line["sparse_step" if other else "dense_step"] = o
     line["accept_commit"] = measure_commit(torch, ops, cfg, x, base, dev)
-    line["importance_scores"] = measure_scores(torch, ops, cfg, base, dev, ms_per_step)
+    line["importance_scores"] = measure_scores(torch, ops, cfg, sets, dev, ms_per_step)
     line["draft_tree"] = measure_tree(torch, ops, cfg, dev)
     if args.copy_calib_gib > 0:
         n = int(args.copy_calib_gib * (1 << 30))

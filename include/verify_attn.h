@@ -252,7 +252,11 @@ va_status importance_scores(const va_score_desc* desc, const void* q, const void
  *   accepted    [B] int32 device: deepest accepted node in [0, N), or -1 for
  *               none (values outside [-1, N) act as -1)
  *   cache_len   [B] int32 device: valid tokens per sequence before the call
- *   new_len     [B] int32 device, written
+ *   new_len     [B] int32 device, written; it must not overlap cache_len,
+ *               accepted or parent (VA_EINVAL): every KV head's workgroup
+ *               reads those while one of them writes new_len, so an
+ *               in-place length update would race.  Update the lengths by
+ *               copying new_len into cache_len after the call.
  * Rows that would land at or past the capacity are not written (new_len
  * still counts them).  Device pointers, asynchronous on `stream`; no
  * workspace.  Malformed parents end a path as in the tree mask. */

@@ -70,6 +70,12 @@ va_status check_desc(const va_attn_desc* d) {
 
 bool misaligned(const void* p) { return ((uintptr_t)p & 15u) != 0; }
 
+// Byte ranges [a, a + na) and [b, b + nb) share an address.
+bool overlaps(const void* a, int64_t na, const void* b, int64_t nb) {
+  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return x < y + (uintptr_t)nb && y < x + (uintptr_t)na;
+}
+
 va::Plan make_plan(const va_attn_desc* d, int32_t n_ctx) {
   va::Plan pl{};
   const int G = d->Hq / d->Hkv;
@@ -292,6 +298,15 @@ va_status accept_commit(const va_attn_desc* desc, void* k_cache, void* v_cache, 
   if (st != VA_OK) return st;
   if (!k_cache || !v_cache || !k_draft || !v_draft || !parent || !accepted || !cache_len || !new_len)
     return fail(VA_EINVAL, "every tensor of accept_commit must be non-NULL");
+  // Every workgroup of a sequence reads cache_len[b], accepted[b] and its
+  // parent row, while one of them writes new_len[b]: an in-place length
+  // update would race with the other KV heads' reads.
+  {
+    const int64_t nb = (int64_t)desc->B * 4;
+    if (overlaps(new_len, nb, cache_len, nb) || overlaps(new_len, nb, accepted, nb) ||
+        overlaps(new_len, nb, parent, nb * desc->N))
+      return fail(VA_EINVAL, "new_len must not overlap cache_len, accepted or parent");
+  }
   if (misaligned(k_cache) || misaligned(v_cache) || misaligned(k_draft) || misaligned(v_draft))
     return fail(VA_EINVAL, "tensor base pointers must be 16-byte aligned");
   va::CommitParams p{};

@@ -30,6 +30,9 @@ __global__ __launch_bounds__(kCommitThreads) void commit_kernel(CommitParams p) 
   const int b = blockIdx.x / p.Hkv;
   // the parent row in one coalesced read, then the walk in LDS
   for (int j = threadIdx.x; j < p.N; j += kCommitThreads) par[j] = p.parent[(int64_t)b * p.N + j];
+  // The sequence's length is read before any store of this launch (the host
+  // rejects an output length array that overlaps an input).
+  const int base = p.cache_len[b];
   __syncthreads();
   if (threadIdx.x == 0) {
     const int leaf = p.accepted[b];
@@ -48,11 +51,10 @@ __global__ __launch_bounds__(kCommitThreads) void commit_kernel(CommitParams p) 
       }
     }
     plen = n;
-    if (kvh == 0) p.new_len[b] = p.cache_len[b] + n;
+    if (kvh == 0) p.new_len[b] = base + n;
   }
   __syncthreads();
   const int n = plen;
-  const int base = p.cache_len[b];
   const int chunks = p.row_bytes / 16;
   unsigned char* kc = (unsigned char*)p.kc;
   unsigned char* vc = (unsigned char*)p.vc;

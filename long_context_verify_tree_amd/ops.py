@@ -109,6 +109,12 @@ def _dtype_code(t: torch.Tensor) -> int:
     raise TypeError(f"unsupported dtype {t.dtype}")
 
 
+def _row_stride(t: torch.Tensor, row_len: int) -> int:
+    """Row stride of a [B, n] tensor; a single row may carry any stride (a
+    broadcast view has 0), and its length stands in for it."""
+    return t.stride(0) if t.shape[0] > 1 else row_len
+
+
 def _strides3(t: torch.Tensor):
     if t.dim() != 4 or t.stride(3) != 1:
         raise ValueError("tensors must be 4-D with a unit innermost stride")
@@ -196,7 +202,8 @@ def verify_attn_sparse(q, k_cache, v_cache, k_draft, v_draft, parent, verify_idx
     """Sparse verification over verify_idx [B, K] int32; returns (out, lse)."""
     load()
     _check_inputs(q, k_cache, v_cache, k_draft, v_draft, parent)
-    if verify_idx.dtype != torch.int32 or verify_idx.dim() != 2 or verify_idx.stride(1) != 1:
+    if verify_idx.dtype != torch.int32 or verify_idx.dim() != 2 or \
+            (verify_idx.shape[1] > 1 and verify_idx.stride(1) != 1):
         raise ValueError("verify_idx must be int32 [B, K] with unit column stride")
     K = verify_idx.shape[1]
     out, lse = _outputs(q, out, lse, want_lse)
@@ -204,7 +211,7 @@ def verify_attn_sparse(q, k_cache, v_cache, k_draft, v_draft, parent, verify_idx
     ws = _workspace(desc, K, q.device, workspace)
     _check(_lib.verify_attn_sparse(ctypes.byref(desc), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_draft),
                                    _ptr(v_draft), _ptr(parent), _ptr(verify_idx), K,
-                                   verify_idx.stride(0) if K else 0, _ptr(out), _ptr(lse), _ptr(ws),
+                                   _row_stride(verify_idx, K) if K else 0, _ptr(out), _ptr(lse), _ptr(ws),
                                    ws.numel(), _stream(q.device)))
     return out, lse
 
@@ -214,7 +221,7 @@ def verify_attn_partials(desc: AttnDesc, q, k_cache, v_cache, k_draft, v_draft, 
     """First stage only (split partials + tree partial) into ``workspace``."""
     load()
     K = verify_idx.shape[1] if verify_idx is not None else desc.L
-    stride = verify_idx.stride(0) if verify_idx is not None else 0
+    stride = _row_stride(verify_idx, K) if verify_idx is not None else 0
     _check(_lib.verify_attn_partials(ctypes.byref(desc), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_draft),
                                      _ptr(v_draft), _ptr(parent), _ptr(verify_idx), K, stride, _ptr(workspace),
                                      workspace.numel(), _stream(q.device)))
@@ -242,16 +249,17 @@ def select_verify_set(draft_score, target_score, *, sink: int, window: int, top_
         raise ValueError("scores must both be [B, L]")
     if draft_score.dtype != torch.float32 or target_score.dtype != torch.float32:
         raise ValueError("scores must be float32")
-    if draft_score.stride(1) != 1 or target_score.stride(1) != 1 or draft_score.stride(0) != target_score.stride(0):
-        raise ValueError("score rows must be contiguous with a common row stride")
     B, L = draft_score.shape
+    if draft_score.stride(1) != 1 or target_score.stride(1) != 1 or \
+            _row_stride(draft_score, L) != _row_stride(target_score, L):
+        raise ValueError("score rows must be contiguous with a common row stride")
     k_out = min(budget, L)
     if out is None:
         out = torch.empty((B, k_out), dtype=torch.int32, device=draft_score.device)
     need = select_workspace_size(B, L)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=draft_score.device)
-    _check(_lib.select_verify_set(_ptr(draft_score), _ptr(target_score), B, L, draft_score.stride(0) if B else L,
+    _check(_lib.select_verify_set(_ptr(draft_score), _ptr(target_score), B, L, _row_stride(draft_score, L) if B else L,
                                   sink, window, top_m, budget, _ptr(out), _ptr(workspace),
                                   workspace.numel() if workspace is not None else 0,
                                   _stream(draft_score.device)))
@@ -298,7 +306,8 @@ def importance_scores(q, k, scale: Optional[float] = None, out=None, workspace=N
         raise ValueError("out must be float32 with contiguous rows")
     if workspace is None:
         workspace = torch.empty(scores_workspace_size(desc), dtype=torch.uint8, device=q.device)
-    _check(_lib.importance_scores(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(out), out.stride(0), _ptr(workspace),
+    _check(_lib.importance_scores(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(out), _row_stride(out, desc.L),
+                                  _ptr(workspace),
                                   workspace.numel(), _stream(q.device)))
     return out
 
@@ -343,6 +352,10 @@ def accept_commit(k_cache, v_cache, k_draft, v_draft, parent, accepted, cache_le
             raise ValueError("parent [B, N], accepted [B] and cache_len [B] expected")
     if new_len is None:
         new_len = torch.empty(desc.B, dtype=torch.int32, device=k_cache.device)
+    for t, name in ((cache_len, "cache_len"), (accepted, "accepted"), (parent, "parent")):
+        lo, hi = t.data_ptr(), t.data_ptr() + t.numel() * t.element_size()
+        if new_len.data_ptr() < hi and lo < new_len.data_ptr() + new_len.numel() * 4:
+            raise ValueError(f"new_len must not overlap {name} (the library rejects in-place length updates)")
     _check(_lib.accept_commit(ctypes.byref(desc), _ptr(k_cache), _ptr(v_cache), _ptr(k_draft), _ptr(v_draft),
                               _ptr(parent), _ptr(accepted), _ptr(cache_len), _ptr(new_len), _stream(k_cache.device)))
     return new_len

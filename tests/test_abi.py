@@ -194,6 +194,27 @@ def test_commit_rejects_before_launch(ops):
     assert f(ctypes.byref(d), *args, None) == ops.VA_EUNSUPPORTED
 
 
+def test_commit_rejects_aliased_lengths(ops):
+    # new_len written in place of cache_len, accepted or the parent rows would
+    # race with the other KV heads' reads: rejected on the host
+    d = good_desc(ops)                      # B = 2, N = 8
+    f = ops._lib.accept_commit
+    base = 0x200000
+    P = lambda off: ctypes.c_void_p(base + off)
+    kc, vc, kd, vd = P(0x10000), P(0x20000), P(0x30000), P(0x40000)
+    parent, accepted, cache_len = P(0x1000), P(0x2000), P(0x3000)
+    ok_new = P(0x4000)
+    for new in (cache_len, P(0x3000 + 4), P(0x3000 - 4), accepted, P(0x1000 + 60)):
+        assert f(ctypes.byref(d), kc, vc, kd, vd, parent, accepted, cache_len, new, None) == ops.VA_EINVAL
+        assert b"overlap" in ops._lib.va_last_error()
+    # adjacent but disjoint ranges pass the overlap check; a misaligned cache
+    # (checked after it) stops the call before any launch
+    bad_kc = P(0x10004)
+    for new in (P(0x3000 + 8), P(0x3000 - 8), ok_new):
+        assert f(ctypes.byref(d), bad_kc, vc, kd, vd, parent, accepted, cache_len, new, None) == ops.VA_EINVAL
+        assert b"aligned" in ops._lib.va_last_error()
+
+
 def test_tree_rejects_before_launch(ops):
     f = ops._lib.build_draft_tree
     ok_args = (FAKE, FAKE, 2, 4, 3, 10, FAKE, FAKE, FAKE, FAKE, None)

@@ -305,14 +305,19 @@ def full_inputs():
     return get
 
 
-def _pairs(cfg, rng, k=3):
+def _pairs(cfg, rng):
+    """(sequence, query head) pairs checked at full size: one query head of
+    every (sequence, KV head) work item (a seeded choice within the group),
+    plus the first and the last head of the whole batch."""
     pairs = {(0, 0), (cfg.B - 1, cfg.Hq - 1)}
-    while len(pairs) < k:
-        pairs.add((int(rng.integers(cfg.B)), int(rng.integers(cfg.Hq))))
+    for b in range(cfg.B):
+        for kvh in range(cfg.Hkv):
+            pairs.add((b, kvh * cfg.G + int(rng.integers(cfg.G))))
     return sorted(pairs)
 
 
-@pytest.mark.parametrize("name", ["llama3_8b_chain8_L32k", "llama3_8b_tree64_L64k", "l70b_tree128_L128k"])
+@pytest.mark.parametrize("name", ["llama3_8b_chain8_L32k", "llama3_8b_tree64_L64k", "l70b_tree128_L128k",
+                                  "qwen25_7b_sparse2048_L32k"])
 def test_full_size_dense_sampled(gpu_lib, full_inputs, name):
     x = full_inputs(name)
     cfg = x.cfg
@@ -320,6 +325,8 @@ def test_full_size_dense_sampled(gpu_lib, full_inputs, name):
     got, glse = gpu_dense(gpu_lib, x)
     assert np.isfinite(got).all()
     pairs = _pairs(cfg, np.random.default_rng(cfg.seed))
+    assert {(b, h // cfg.G) for b, h in pairs} == {(b, k) for b in range(cfg.B) for k in range(cfg.Hkv)}
+    say(f"  oracle on {len(pairs)} (sequence, head) slabs")
     ref, rlse = vo.verify_attention(x.q, x.k_cache, x.v_cache, x.k_draft, x.v_draft, x.parent, heads=pairs)
     for n, (b, h) in enumerate(pairs):
         check_rows(got[b, h], ref[n], glse[b, h], rlse[n], cfg.dtype, f"{name} b={b} h={h}")
@@ -336,6 +343,7 @@ def test_full_size_sparse_sampled(gpu_lib, full_inputs, name):
     say(f"case full sparse {name} K={idx.shape[1]}")
     got, glse = gpu_sparse(gpu_lib, x, idx)
     pairs = _pairs(cfg, np.random.default_rng(cfg.seed + 1))
+    say(f"  oracle on {len(pairs)} (sequence, head) slabs")
     ref, rlse = vo.verify_attention(x.q, x.k_cache, x.v_cache, x.k_draft, x.v_draft, x.parent, ctx_index=idx,
                                     heads=pairs)
     for n, (b, h) in enumerate(pairs):

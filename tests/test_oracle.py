@@ -678,6 +678,80 @@ def test_tree_is_the_top_n_prefixes_by_brute_force(seed, K, T, N):
     np.testing.assert_allclose(a_hat, rho.astype(np.float64).sum(), rtol=1e-6)
 
 
+def _full_frontier_tree(prob, tok, N):
+    """The best-first expansion written out plainly: at every step consider
+    every child not yet in the tree of every node already in it (and of the
+    virtual root), take the largest path score rho; equal rho goes to the
+    child of the node that entered the tree first (the root before every
+    node), then to the better ranked candidate (higher probability, then
+    lower candidate index).  rho is a float32 product, parent first; NaN and
+    negative probabilities count as 0."""
+    prob = np.asarray(prob, dtype=np.float32)
+    K, T = prob.shape
+    q = [[float(prob[k, c]) if prob[k, c] > 0 else 0.0 for c in range(T)] for k in range(K)]
+    rank = [{c: r for r, c in enumerate(sorted(range(T), key=lambda c: (-q[k][c], c)))} for k in range(K)]
+    nodes = []                       # (parent, candidate, depth, rho)
+    used = set()                     # (parent, candidate) pairs in the tree
+    while len(nodes) < N:
+        best = None
+        for p in [-1] + list(range(len(nodes))):
+            depth = 0 if p == -1 else nodes[p][2]
+            if depth >= K:
+                continue
+            rho_p = np.float32(1.0) if p == -1 else nodes[p][3]
+            for c in range(T):
+                if (p, c) in used:
+                    continue
+                r = np.float32(rho_p * np.float32(q[depth][c]))
+                key = (-float(r), p, rank[depth][c])
+                if best is None or key < best[0]:
+                    best = (key, p, c, depth + 1, r)
+        _, p, c, d, r = best
+        used.add((p, c))
+        nodes.append((p, c, d, r))
+    parent = np.array([n[0] for n in nodes], dtype=np.int32)
+    token = np.array([tok[n[2] - 1][n[1]] for n in nodes], dtype=np.int32)
+    rho = np.array([n[3] for n in nodes], dtype=np.float32)
+    return parent, token, rho
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_tree_matches_a_full_frontier_scan_under_ties(seed):
+    # probabilities drawn from a few dyadic levels (and 0, NaN, negatives), so
+    # that equal path scores across parents and within a parent are common:
+    # the node order under ties is pinned, not only the node set
+    rng = np.random.default_rng(seed)
+    levels = np.array([0.5, 0.25, 0.25, 0.125, 1.0, 0.0, np.nan, -0.5], dtype=np.float32)
+    for _ in range(25):
+        K, T = int(rng.integers(1, 5)), int(rng.integers(1, 5))
+        prob = levels[rng.integers(0, 5 if seed % 3 else len(levels), (K, T))]
+        tok = rng.integers(0, 50, (K, T)).astype(np.int32)
+        total = sum(T ** d for d in range(1, K + 1))
+        N = int(rng.integers(1, min(total, 40) + 1))
+        want = _full_frontier_tree(prob, tok, N)
+        parent, token, rho, a_hat = vo.best_first_tree(prob, tok, N)
+        np.testing.assert_array_equal(parent, want[0])
+        np.testing.assert_array_equal(token, want[1])
+        np.testing.assert_array_equal(rho, want[2])
+        s = np.float32(0)
+        for r in want[2]:
+            s = np.float32(s + r)
+        assert a_hat == s
+
+
+def test_full_frontier_scan_hand_example():
+    # the plain scan itself on a hand-worked case: K = 2, T = 2,
+    # q0 = (0.5, 0.25), q1 = (0.5, 0.5).  rho: root children 0.5, 0.25;
+    # children of node 0: 0.25, 0.25; of node 1: 0.125, 0.125.  Ties at 0.25:
+    # the root's child (parent -1) first, then node 0's two children.
+    prob = np.array([[0.5, 0.25], [0.5, 0.5]], dtype=np.float32)
+    tok = np.array([[1, 2], [3, 4]], dtype=np.int32)
+    parent, token, rho = _full_frontier_tree(prob, tok, 6)
+    assert list(parent) == [-1, -1, 0, 0, 1, 1]
+    assert list(token) == [1, 2, 3, 4, 3, 4]
+    assert list(rho) == [0.5, 0.25, 0.25, 0.25, 0.125, 0.125]
+
+
 def test_tree_equal_probabilities_hand_order():
     # K=2, T=2, every q = 1/2: the root's two candidates (rho 1/2) come
     # first, then the children of node 0 (parent 0 before parent 1), then
