@@ -126,6 +126,26 @@ va_status verify_attn_dense(const va_attn_desc* desc,
                             void* out, float* lse,
                             void* ws, size_t ws_bytes, void* stream);
 
+/* verify_attn_dense without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  The split partials go to a fixed
+ * device array of va_noalloc_scratch_bytes() (64 MiB) that the library
+ * holds on each GPU it runs on until the process ends; the call allocates
+ * nothing.  Shapes whose partials need more than that return VA_EWORKSPACE
+ * (use verify_attn_dense).  Every call on one GPU shares that GPU's array:
+ * calls that overlap in time on one GPU (several streams, or threads)
+ * race and must be serialised by the caller.  The device is the stream's
+ * (the current device for a NULL stream).  Other arguments as for
+ * verify_attn_dense; results are bitwise those of verify_attn_dense. */
+va_status verify_attn_dense_noalloc(const va_attn_desc* desc,
+                                    const void* q, const void* k_cache, const void* v_cache,
+                                    const void* k_draft, const void* v_draft,
+                                    const int32_t* parent,
+                                    void* out, float* lse, void* stream);
+
+/* Size in bytes of the fixed scratch of verify_attn_dense_noalloc. */
+size_t va_noalloc_scratch_bytes(void);
+
 /* Sparse verification: context part over the verify set only.
  *   verify_idx  [B, K] int32, row stride idx_stride (>= K); each row holds K
  *               distinct token positions in [0, L) (any order; ascending is

@@ -9,6 +9,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
 #include <hip/hip_runtime.h>
 
 #include "../../include/verify_attn.h"
@@ -203,9 +205,72 @@ va_status run_merge(const va_attn_desc* d, int32_t n_ctx, void* out, float* lse,
   return ok();
 }
 
+// Fixed device scratch of verify_attn_dense_noalloc: the split partials
+// (normalised partial rows and their log2-sum-exps) of one call.  Each GPU
+// the library runs on holds its own copy until the process ends; its device
+// address is looked up once per device (the name itself is a host-side
+// stand-in and is never passed to a kernel or a copy).
+constexpr size_t kScratchBytes = (size_t)64 << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on device dev (looked up on the first call on
+// that device, with dev current); nullptr and a message on failure.
+void* scratch_on(int dev, va_status* st) {
+  if (dev < 0 || dev >= kMaxDevices) {
+    *st = fail(VA_EUNSUPPORTED, "device %d beyond the %d devices the fixed scratch serves", dev, kMaxDevices);
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    int cur = -1;
+    hipError_t e = hipGetDevice(&cur);
+    if (e == hipSuccess && cur != dev) e = hipSetDevice(dev);
+    void* ptr = nullptr;
+    if (e == hipSuccess) e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (cur >= 0 && cur != dev) {
+      const hipError_t e2 = hipSetDevice(cur);
+      if (e == hipSuccess) e = e2;
+    }
+    if (e != hipSuccess || ptr == nullptr) {
+      *st = fail(VA_EHIP, "looking up the fixed scratch on device %d: %s", dev, hipGetErrorString(e));
+      return nullptr;
+    }
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+
 }  // namespace
 
 extern "C" {
+
+va_status verify_attn_dense_noalloc(const va_attn_desc* desc, const void* q, const void* k_cache,
+                                    const void* v_cache, const void* k_draft, const void* v_draft,
+                                    const int32_t* parent, void* out, float* lse, void* stream) {
+  va_status st = check_desc(desc);
+  if (st != VA_OK) return st;
+  if (!out) return fail(VA_EINVAL, "out must be non-NULL");
+  if (misaligned(out)) return fail(VA_EINVAL, "out must be 16-byte aligned");
+  const size_t need = make_plan(desc, desc->L).ws_bytes;
+  if (need > kScratchBytes)
+    return fail(VA_EWORKSPACE, "this shape needs %zu bytes of partials, beyond the fixed scratch of %zu bytes "
+                "(use verify_attn_dense with a caller workspace)", need, kScratchBytes);
+  int dev = -1;
+  hipError_t e = stream != nullptr ? hipStreamGetDevice((hipStream_t)stream, &dev) : hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(VA_EHIP, "device of the stream: %s", hipGetErrorString(e));
+  void* ws = scratch_on(dev, &st);
+  if (ws == nullptr) return st;
+  st = run_partials(desc, q, k_cache, v_cache, k_draft, v_draft, parent, false, nullptr, desc->L, 0, ws,
+                    kScratchBytes, (hipStream_t)stream);
+  if (st != VA_OK) return st;
+  return run_merge(desc, desc->L, out, lse, ws, kScratchBytes, (hipStream_t)stream);
+}
+
+size_t va_noalloc_scratch_bytes(void) { return kScratchBytes; }
 
 va_status va_attn_workspace_size(const va_attn_desc* desc, int32_t n_ctx, size_t* bytes) {
   va_status st = check_desc(desc);

@@ -57,6 +57,8 @@ def _declare(lib):
         "verify_attn_sparse": (i32, [_DESC_P, _P, _P, _P, _P, _P, _P, _P, i32, i64, _P, _P, _P, sz, _P]),
         "verify_attn_partials": (i32, [_DESC_P, _P, _P, _P, _P, _P, _P, _P, i32, i64, _P, sz, _P]),
         "verify_attn_merge": (i32, [_DESC_P, i32, _P, _P, _P, sz, _P]),
+        "verify_attn_dense_noalloc": (i32, [_DESC_P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
+        "va_noalloc_scratch_bytes": (sz, []),
         "va_select_workspace_size": (i32, [i32, i32, ctypes.POINTER(sz)]),
         "select_verify_set": (i32, [_P, _P, i32, i32, i64, i32, i32, i32, i32, _P, _P, sz, _P]),
         "accept_commit": (i32, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
@@ -194,6 +196,26 @@ def verify_attn_dense(q, k_cache, v_cache, k_draft, v_draft, parent, *, out=None
                                   _ptr(v_draft), _ptr(parent), _ptr(out), _ptr(lse), _ptr(ws),
                                   ws.numel(), _stream(q.device)))
     return out, lse
+
+
+def verify_attn_dense_noalloc(q, k_cache, v_cache, k_draft, v_draft, parent, *, out=None, lse=None,
+                              scale: Optional[float] = None,
+                              want_lse: bool = True) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Dense verification through the library's fixed device scratch (no
+    workspace; the library allocates nothing).  Calls on one GPU share that
+    scratch and must not overlap in time."""
+    load()
+    _check_inputs(q, k_cache, v_cache, k_draft, v_draft, parent)
+    out, lse = _outputs(q, out, lse, want_lse)
+    desc = make_desc(q, k_cache, v_cache, k_draft, v_draft, out, scale)
+    _check(_lib.verify_attn_dense_noalloc(ctypes.byref(desc), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_draft),
+                                          _ptr(v_draft), _ptr(parent), _ptr(out), _ptr(lse), _stream(q.device)))
+    return out, lse
+
+
+def noalloc_scratch_bytes() -> int:
+    load()
+    return int(_lib.va_noalloc_scratch_bytes())
 
 
 def verify_attn_sparse(q, k_cache, v_cache, k_draft, v_draft, parent, verify_idx, *, out=None, lse=None,
