@@ -298,7 +298,16 @@ va_status va_select_workspace_size(int32_t B, int32_t L, size_t* bytes);
  *   ws          device workspace of va_select_workspace_size(B, L) bytes
  * budget >= L returns every index 0..L-1.  With budget < L, rows longer
  * than 786432 tokens (24 x 32768) return VA_EUNSUPPORTED: each row's token
- * marks are kept on chip. */
+ * marks are kept on chip.
+ * Rows longer than 32768 tokens of a batch whose 16384-token workgroups
+ * (B * ceil(L / 16384) of them, at most 256) the device holds at once (by
+ * the occupancy API) are split over several workgroups that wait for one
+ * another; other batches take one workgroup per row.  Every such wait is
+ * bounded, since work on other streams can hold CUs: should one time out,
+ * that row of verify_idx is filled with -1 (never a
+ * valid index; verify_attn_sparse stays memory-safe on it, with an
+ * unspecified result), so a row whose first entry is -1 must not be used
+ * as a verify set. */
 va_status select_verify_set(const float* draft_score, const float* target_score,
                             int32_t B, int32_t L, int64_t ld,
                             int32_t sink, int32_t window, int32_t top_m, int32_t budget,

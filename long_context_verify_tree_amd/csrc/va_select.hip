@@ -27,6 +27,9 @@
 // several workgroups per row, each holding 16384 tokens in registers.
 
 #include <stdint.h>
+#include <stdlib.h>
+
+#include <atomic>
 
 #include <hip/hip_runtime.h>
 
@@ -323,10 +326,15 @@ __global__ __launch_bounds__(kST) void select_kernel(SelParams p) {
 //   * the counts of equal keys and of output tokens are published per
 //     segment, so each workgroup knows how many precede it in index order.
 // A row barrier is an arrival counter in the workspace: each workgroup adds
-// one and waits until all P have arrived for this phase.  The wait is
-// bounded (a flag in the workspace records a timeout), so every wave exits;
-// the launch is used only when all B * P workgroups fit on the device at
-// once, which the waits rely on.
+// one and waits until all P have arrived for this phase.  The waits rely on
+// every workgroup of the launch being resident at once: the host takes this
+// kernel only when the occupancy API says the device holds B * P of its
+// workgroups at once (else one workgroup per row).  Work on other streams
+// can still hold CUs, so each wait is bounded: a timeout sets the row's
+// error flag and the wave moves on, so every wave exits; the last workgroup
+// of the row to finish (a counter bumped once its output stores are
+// performed) then overwrites the whole row with -1, which the caller sees in
+// place of a verify set.
 
 #ifndef VA_SEL_CT
 #define VA_SEL_CT 512   // 128: 83 us, 256: 64 us, 512: 58 us, 1024: 69 us on 4 rows of 131072
@@ -343,6 +351,7 @@ constexpr int kWsHt = kBins0;              // first digit, target tier [kBins0]
 constexpr int kWsHp = 2 * kBins0;          // later digits [tier][pass - 1][1024]
 constexpr int kWsBar = kWsHp + 4 * 1024;   // arrival counter
 constexpr int kWsErr = kWsBar + 1;         // set when a wait timed out
+constexpr int kWsDone = kWsBar + 2;        // workgroups whose output stores are performed
 constexpr int kWsCnt = kWsBar + 64;        // per segment: equal keys [2][P], output tokens [P]
 
 __host__ __device__ inline int64_t cluster_row_ints(int P) { return ((int64_t)kWsCnt + 3 * P + 63) / 64 * 64; }
@@ -362,14 +371,14 @@ __device__ inline int ld_dev(const int* p) { return __hip_atomic_load(p, __ATOMI
 // read with agent-scope loads, so no cache write-back or invalidation is
 // needed: each wavefront only waits until its own atomics are performed
 // before the workgroup arrives.
-__device__ inline void row_barrier(int* ws, int P, int phase) {
+__device__ inline void row_barrier(int* ws, int P, int phase, int spin_limit) {
   __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
   __syncthreads();
   if (threadIdx.x == 0) {
     __hip_atomic_fetch_add(ws + kWsBar, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const int target = phase * P;
     for (int spin = 0; ld_dev(ws + kWsBar) < target; ++spin) {
-      if (spin == kSpinLimit) {
+      if (spin >= spin_limit) {
         __hip_atomic_store(ws + kWsErr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         break;
       }
@@ -405,7 +414,7 @@ __device__ inline void cpick(const int* hist, int nbins, int r, int above, CShar
   __syncthreads();
 }
 
-__global__ __launch_bounds__(kCT) void select_cluster_kernel(SelParams p, int* ws_all, int P) {
+__global__ __launch_bounds__(kCT) void select_cluster_kernel(SelParams p, int* ws_all, int P, int spin_limit) {
   __shared__ CShared sh;
   const int tid = threadIdx.x;
   const int b = blockIdx.x / P, seg = blockIdx.x % P;
@@ -467,7 +476,7 @@ __global__ __launch_bounds__(kCT) void select_cluster_kernel(SelParams p, int* w
     if (sh.ha[i]) atomicAdd(ws + kWsHd + i, sh.ha[i]);
     if (sh.hb[i]) atomicAdd(ws + kWsHt + i, sh.hb[i]);
   }
-  row_barrier(ws, P, ++phase);
+  row_barrier(ws, P, ++phase, spin_limit);
 
   // Marks the top r candidates (free, not yet marked) of tier ti, whose
   // row-wide first-digit histogram is g0.
@@ -493,7 +502,7 @@ __global__ __launch_bounds__(kCT) void select_cluster_kernel(SelParams p, int* w
       __syncthreads();
       for (int i = tid; i < nb; i += kCT)
         if (sh.hb[i]) atomicAdd(gp + i, sh.hb[i]);
-      row_barrier(ws, P, ++phase);
+      row_barrier(ws, P, ++phase, spin_limit);
       for (int i = tid; i < nb; i += kCT) sh.ha[i] = ld_dev(gp + i);
       __syncthreads();
       cpick(sh.ha, nb, r, above, sh);
@@ -515,7 +524,7 @@ __global__ __launch_bounds__(kCT) void select_cluster_kernel(SelParams p, int* w
     int tot;
     const int before = block_excl_scan<true, kCWaves>(__popc(eq), sh.wsum, &tot);
     if (tid == 0) __hip_atomic_store(ws + kWsCnt + ti * P + seg, tot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    row_barrier(ws, P, ++phase);
+    row_barrier(ws, P, ++phase, spin_limit);
     int prev = 0;   // equal keys in earlier segments
     for (int q = tid; q < seg; q += kCT) prev += ld_dev(ws + kWsCnt + ti * P + q);
     int earlier;
@@ -533,7 +542,7 @@ __global__ __launch_bounds__(kCT) void select_cluster_kernel(SelParams p, int* w
 #pragma unroll
       for (int i = 0; i < kKPT; ++i)
         if ((mark >> i) & 1u) atomicSub(ws + kWsHt + (kt[i] >> kDigitShift[0]), 1);
-      row_barrier(ws, P, ++phase);
+      row_barrier(ws, P, ++phase, spin_limit);
     }
     tier(1, r2, ws + kWsHt, kt);
   }
@@ -544,7 +553,7 @@ __global__ __launch_bounds__(kCT) void select_cluster_kernel(SelParams p, int* w
   int tot;
   const int before = block_excl_scan<true, kCWaves>(__popc(sel), sh.wsum, &tot);
   if (tid == 0) __hip_atomic_store(ws + kWsCnt + 2 * P + seg, tot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  row_barrier(ws, P, ++phase);
+  row_barrier(ws, P, ++phase, spin_limit);
   int prev = 0;
   for (int q = tid; q < seg; q += kCT) prev += ld_dev(ws + kWsCnt + 2 * P + q);
   int earlier;
@@ -552,8 +561,19 @@ __global__ __launch_bounds__(kCT) void select_cluster_kernel(SelParams p, int* w
   int pos = earlier + before;
   for (uint32_t e = sel; e; e &= e - 1) {
     const int i = __ffs(e) - 1;
-    if (pos < p.k_out) out[pos] = j0 + i;
+    if (pos < p.k_out) __hip_atomic_store(out + pos, j0 + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     ++pos;
+  }
+  // The last workgroup of the row to get here sees every other workgroup's
+  // output stores performed (agent-scope stores, performed before each
+  // workgroup's count): if any wait of the row timed out, the row is
+  // replaced by -1.
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+  __syncthreads();
+  if (tid == 0) sh.pick[0] = __hip_atomic_fetch_add(ws + kWsDone, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  if (sh.pick[0] == P - 1 && ld_dev(ws + kWsErr) != 0) {
+    for (int j = tid; j < p.k_out; j += kCT) __hip_atomic_store(out + j, -1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
@@ -571,6 +591,40 @@ __global__ __launch_bounds__(256) void zero_ints_kernel(int* p, int64_t n) {
 inline int cluster_parts(int32_t B, int32_t L) {
   const int P = (int)(((int64_t)L + kCSeg - 1) / kCSeg);
   return L > kSeg && (int64_t)B * P <= kCMaxGroups ? P : 0;
+}
+
+// Workgroups of select_cluster_kernel that the current device holds at once
+// (occupancy per CU times CUs; 0 if it cannot be queried), looked up once
+// per device.
+int cluster_capacity() {
+  constexpr int kDevs = 64;
+  static std::atomic<int> cache[kDevs];   // 0: not looked up yet; else capacity + 1
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (dev >= 0 && dev < kDevs) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c - 1;
+  }
+  int cus = 0, per_cu = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)select_cluster_kernel, kCT, 0) !=
+          hipSuccess) {
+    (void)hipGetLastError();
+    return 0;
+  }
+  const int cap = cus * per_cu;
+  if (dev >= 0 && dev < kDevs) cache[dev].store(cap + 1, std::memory_order_relaxed);
+  return cap;
+}
+
+// Polls per row-barrier wait: kSpinLimit, or VA_SELECT_SPIN_LIMIT from the
+// environment (a test hook: a limit of 0 makes every early arrival give up
+// at once, which exercises the timeout path).
+int spin_limit() {
+  const char* e = getenv("VA_SELECT_SPIN_LIMIT");
+  if (e == nullptr || *e == '\0') return kSpinLimit;
+  const long v = strtol(e, nullptr, 10);
+  return v < 0 ? 0 : (v > kSpinLimit ? kSpinLimit : (int)v);
 }
 
 }  // namespace
@@ -594,14 +648,19 @@ hipError_t launch_select(const float* draft_score, const float* target_score, in
   p.top_m = top_m;
   p.budget = budget;
   p.k_out = budget < L ? budget : L;
-  const int P = budget < L ? cluster_parts(B, L) : 0;
+  int P = budget < L ? cluster_parts(B, L) : 0;
+  if (P && cluster_capacity() < B * P) P = 0;   // not every workgroup would be resident
   if (P) {
     const int64_t n = (int64_t)B * cluster_row_ints(P);
     const int grid = (int)((n + 255) / 256 < 1024 ? (n + 255) / 256 : 1024);
     hipLaunchKernelGGL(zero_ints_kernel, dim3(grid), dim3(256), 0, stream, (int*)ws, n);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(select_cluster_kernel, dim3(B * P), dim3(kCT), 0, stream, p, (int*)ws, P);
+    int* ws_i = (int*)ws;
+    int lim = spin_limit();
+    // (a cooperative launch, which would have the runtime guarantee
+    // co-residency, cost ~20 us per call: 56 -> 76 us on 4 rows of 131072)
+    hipLaunchKernelGGL(select_cluster_kernel, dim3(B * P), dim3(kCT), 0, stream, p, ws_i, P, lim);
     return hipGetLastError();
   }
   const int nseg = (L + kSeg - 1) / kSeg;

@@ -288,6 +288,34 @@ def test_selector_ties_specials_and_special_cases(gpu_lib):
             np.testing.assert_array_equal(got, vo.select_verify_set(d, t, 2, 2, budget // 2, budget))
 
 
+def test_multi_workgroup_selector_reports_a_timed_out_wait(gpu_lib, monkeypatch):
+    # 4 rows of 131072 tokens run on 8 workgroups per row that wait for one
+    # another.  With the test hook VA_SELECT_SPIN_LIMIT=0 every workgroup that
+    # arrives at a row barrier before the last one gives up at once: the
+    # kernel still ends normally and the row comes back as -1 (never a
+    # silently wrong verify set).  Without the hook the rows equal the oracle.
+    rng = np.random.default_rng(21)
+    d = rng.lognormal(0, 2, (4, 131072)).astype(np.float32)
+    t = rng.lognormal(0, 2, (4, 131072)).astype(np.float32)
+    ref = vo.select_verify_set(d, t, 4, 256, 2048, 4096)
+    say("case cluster selector, normal waits")
+    np.testing.assert_array_equal(_sel_gpu(gpu_lib, d, t, 4, 256, 2048, 4096), ref)
+    monkeypatch.setenv("VA_SELECT_SPIN_LIMIT", "0")
+    flagged = 0
+    for rep in range(3):
+        say(f"case cluster selector, waits that give up at once ({rep})")
+        got = _sel_gpu(gpu_lib, d, t, 4, 256, 2048, 4096)
+        for b in range(4):
+            if (got[b] == -1).all():
+                flagged += 1
+            else:
+                np.testing.assert_array_equal(got[b], ref[b])
+    assert flagged > 0
+    monkeypatch.delenv("VA_SELECT_SPIN_LIMIT")
+    say("case cluster selector, normal waits again")
+    np.testing.assert_array_equal(_sel_gpu(gpu_lib, d, t, 4, 256, 2048, 4096), ref)
+
+
 # ---------------------------------------------------------------------------
 # full workload sizes, sampled slabs
 
