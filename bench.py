@@ -350,14 +350,16 @@ def measure_tree(torch, ops, cfg, dev, reps: int = 20):
             "mean_a_hat": round(float(res[3].mean().item()), 4), "kernel": "tree_kernel"}
 
 
-SWEEP_N = (1, 2, 4, 8, 16, 32, 64, 96, 128, 192, 256)
+SWEEP_N = (1, 2, 4, 8, 12, 16, 17, 24, 32, 48, 64, 65, 96, 128, 129, 160, 192, 224, 256)
 
 
 def sweep_n(args):
     """T_verify(N) on the workload's context (K/V cache, batch, heads) for
     best-first trees of N nodes built from synthetic drafter candidates;
-    least-squares calibration of the roofline model's bandwidth, compute and
-    overhead; the controller's tree size on the trees' surrogate curve."""
+    least-squares calibration of the library's plan-following time model
+    (bandwidth, the two kernels' compute rates, overhead); the knee where the
+    model turns compute-bound; the controller's tree size on the trees'
+    surrogate curve."""
     import torch
     from scipy.optimize import least_squares
     from long_context_verify_tree_amd import ops, synth
@@ -370,7 +372,6 @@ def sweep_n(args):
     g.manual_seed(cfg.seed)
     dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
     B, Hq, Hkv, D, L = cfg.B, cfg.Hq, cfg.Hkv, cfg.D, cfg.L
-    e = 2 if cfg.dtype == "bf16" else 4
     kc = torch.randn(B, Hkv, L, D, device=dev, generator=g).to(dt)
     vc = torch.randn(B, Hkv, L, D, device=dev, generator=g).to(dt)
     # best-first trees of up to 256 nodes from seeded drafter candidates
@@ -402,38 +403,47 @@ def sweep_n(args):
         torch.cuda.synchronize()
         times.append((time.perf_counter() - t0) / args.steps)
         print(f"[sweep] N={N}: {times[-1] * 1e3:.4f} ms", file=sys.stderr, flush=True)
-    if cfg.N <= SWEEP_N[-1]:
-        rho_all = ops.build_draft_tree(prob, tok, SWEEP_N[-1])[2].cpu().numpy().astype(np.float64)
+    rho_all = ops.build_draft_tree(prob, tok, SWEEP_N[-1])[2].cpu().numpy().astype(np.float64)
     a_curve = np.cumsum(rho_all.mean(axis=0))          # surrogate of the best-first tree of n nodes
-
-    def nbytes(n):
-        return 2 * B * Hkv * L * D * e + B * Hq * n * D * e + 2 * B * Hkv * n * D * e + B * Hq * n * (D * e + 4)
-
-    def model(p, n):
-        bw, fl, c0 = np.exp(p)
-        return np.maximum(nbytes(n) / bw, 4.0 * B * Hq * n * L * D / fl) + c0
-    ns = np.array(SWEEP_N, dtype=np.float64)
-    ts = np.array(times)
-    fit = least_squares(lambda p: np.log(model(p, ns)) - np.log(ts),
-                        x0=np.log([5e12, 1e15, 5e-6]), bounds=(np.log([1e11, 1e12, 1e-8]), np.log([2e13, 5e15, 1e-2])))
-    bw, fl, c0 = (float(v) for v in np.exp(fit.x))
     desc1 = ops.make_desc(torch.empty(B, Hq, 1, D, dtype=dt, device=dev), kc, vc,
                           torch.empty(B, Hkv, 1, D, dtype=dt, device=dev), torch.empty(B, Hkv, 1, D, dtype=dt, device=dev),
                           torch.empty(B, Hq, 1, D, dtype=dt, device=dev))
+
+    def model(p, ns):
+        bw, cs, ct, c0 = np.exp(p)
+        return np.array([ops.verify_time_model(desc1, L, bw, cs, ct, c0, int(n)) for n in ns])
+    ns = np.array(SWEEP_N)
+    ts = np.array(times)
+    fit = least_squares(lambda p: np.log(model(p, ns)) - np.log(ts), x0=np.log([5e12, 1e15, 4e14, 5e-6]),
+                        bounds=(np.log([1e11, 1e12, 1e12, 1e-8]), np.log([2e13, 5e15, 5e15, 1e-2])))
+    bw, cs, ct, c0 = (float(v) for v in np.exp(fit.x))
     n_all = np.arange(1, SWEEP_N[-1] + 1)
-    t_model = np.array([ops.verify_time_model(desc1, L, bw, fl, c0, int(n)) for n in n_all])
-    knee = int(next((n for n in n_all if 4.0 * B * Hq * n * L * D / fl > nbytes(n) / bw), 0))
+    t_model = model(fit.x, n_all)
+    # knee: the first N whose padded MFMA work outlasts the K/V stream in the fitted model
+    e = 2 if cfg.dtype == "bf16" else 4
+    kv_t = 2.0 * B * Hkv * L * D * e / bw
+    knee = 0
+    for n in n_all:
+        t_no_compute = ops.verify_time_model(desc1, L, bw, 1e30, 1e30, c0, int(n))
+        if t_model[n - 1] > t_no_compute * (1 + 1e-9):
+            knee = int(n)
+            break
     t_ar = float(t_model[0])                           # one autoregressive step's verification
     n_best = ops.choose_tree_size(a_curve, t_model, t_draft=t_ar, l_ar=t_ar)
     S = a_curve * t_ar / (t_ar + t_model)
+    resid = model(fit.x, ns) / ts - 1
     line = {
         "metric": "T_verify(N) sweep + tree-size controller",
-        "workload": cfg.name, "n_ctx_keys": L, "steps": args.steps, "warmup": args.warmup,
+        "workload": cfg.name, "batch": B, "q_heads": Hq, "kv_heads": Hkv, "head_dim": D, "n_ctx_keys": L,
+        "dtype": cfg.dtype, "steps": args.steps, "warmup": args.warmup,
         "N": list(SWEEP_N), "t_verify_ms": [round(t * 1e3, 4) for t in times],
-        "fit": {"bandwidth_gbs": round(bw / 1e9, 1), "compute_tflops": round(fl / 1e12, 1),
-                "overhead_us": round(c0 * 1e6, 2),
-                "max_rel_residual": round(float(np.max(np.abs(model(fit.x, ns) / ts - 1))), 4)},
-        "ridge_knee_N": knee, "measured_read_peak_gbs": read_peak,
+        "t_model_ms": [round(float(t) * 1e3, 4) for t in model(fit.x, ns)],
+        "fit": {"model": "max(KV / bw, padded flops / compute_kernel) + partial rows / bw + overhead (kernel plan)",
+                "bandwidth_gbs": round(bw / 1e9, 1), "compute_shared_tflops": round(cs / 1e12, 1),
+                "compute_tiles_tflops": round(ct / 1e12, 1), "overhead_us": round(c0 * 1e6, 2),
+                "max_rel_residual": round(float(np.max(np.abs(resid))), 4),
+                "kv_stream_ms": round(kv_t * 1e3, 4)},
+        "knee_N": knee, "measured_read_peak_gbs": read_peak,
         "controller": {"t_draft": "= T_verify(1)", "l_ar": "= T_verify(1)", "n_best": n_best,
                        "a_hat_at_n_best": round(float(a_curve[n_best - 1]), 4),
                        "speedup_estimate_at_n_best": round(float(S[n_best - 1]), 4),
@@ -441,6 +451,97 @@ def sweep_n(args):
                                f"{TREE_CANDIDATES} candidates"},
     }
     print(json.dumps(line), flush=True)
+
+
+CROSSOVER_L = (2048, 4096, 8192, 16384, 32768)
+
+
+def score_crossover(args):
+    """Cost of importance estimation against full-cache verification as the
+    context grows (Dustin, "Definizione del Problema": estimators that
+    materialise scores over every head cost more than full attention beyond
+    about 4k tokens; "Metodologia" section 2: scoring a few heads costs a
+    small fraction).  On the workload's head shape, for each L: dense
+    verification (partials + merge), the scoring pass of SCORE_HEADS heads x
+    (up to 32) draft rows, and a naive estimator that scores every query row
+    of every head (the importance map of all Hq * N rows); HIP events on the
+    launching stream, rotated input copies."""
+    import torch
+    from long_context_verify_tree_amd import ops, synth
+
+    ops.load()
+    cfg = synth.CONFIGS[args.config]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    g = torch.Generator(device=dev)
+    g.manual_seed(cfg.seed + 3)
+    dt = torch.bfloat16
+    B, Hq, Hkv, D, N = cfg.B, cfg.Hq, cfg.Hkv, cfg.D, cfg.N
+    G = Hq // Hkv
+    rows_all = G * N
+    reps, copies = 10, 4
+    res = []
+    for L in CROSSOVER_L:
+        sets = []
+        for _ in range(copies):
+            sets.append(dict(q=torch.randn(B, Hq, N, D, device=dev, generator=g).to(dt),
+                             kc=torch.randn(B, Hkv, L, D, device=dev, generator=g).to(dt),
+                             vc=torch.randn(B, Hkv, L, D, device=dev, generator=g).to(dt),
+                             kd=torch.randn(B, Hkv, N, D, device=dev, generator=g).to(dt),
+                             vd=torch.randn(B, Hkv, N, D, device=dev, generator=g).to(dt)))
+        parent = torch.from_numpy(np.tile(np.arange(-1, N - 1, dtype=np.int32), (B, 1))).to(dev)
+        out = torch.empty_like(sets[0]["q"])
+        lse = torch.empty(B, Hq, N, dtype=torch.float32, device=dev)
+        desc = ops.make_desc(sets[0]["q"], sets[0]["kc"], sets[0]["vc"], sets[0]["kd"], sets[0]["vd"], out)
+        ws = torch.empty(ops.workspace_size(desc, L), dtype=torch.uint8, device=dev)
+        hs = min(SCORE_HEADS, Hkv)
+        srow = min(N, 32)
+        sdesc = ops.make_score_desc(sets[0]["q"][:, :hs, :srow], sets[0]["kc"][:, :hs])
+        sws = torch.empty(ops.scores_workspace_size(sdesc), dtype=torch.uint8, device=dev)
+        smap = torch.empty(B, L, dtype=torch.float32, device=dev)
+        # the naive estimator: every query row of every head, 32 rows a call
+        ndescs = []
+        for r0 in range(0, rows_all, 32):
+            qq = sets[0]["q"].reshape(B, Hkv, rows_all, D)[:, 0:1, r0:r0 + 32]
+            ndescs.append((r0, ops.make_score_desc(qq, sets[0]["kc"][:, 0:1])))
+        nws = torch.empty(max(ops.scores_workspace_size(d) for _, d in ndescs), dtype=torch.uint8, device=dev)
+
+        def attn(st):
+            ops.verify_attn_partials(desc, st["q"], st["kc"], st["vc"], st["kd"], st["vd"], parent, ws)
+            ops.verify_attn_merge(desc, L, out, lse, ws)
+
+        def srh(st):
+            ops.importance_scores(st["q"][:, :hs, :srow], st["kc"][:, :hs], out=smap, workspace=sws, desc=sdesc)
+
+        def naive(st):
+            qr = st["q"].reshape(B, Hkv, rows_all, D)
+            for kvh in range(Hkv):
+                for r0, d in ndescs:
+                    ops.importance_scores(qr[:, kvh:kvh + 1, r0:r0 + 32], st["kc"][:, kvh:kvh + 1], out=smap,
+                                          workspace=nws, desc=d)
+
+        def timed(fn):
+            for i in range(3):
+                fn(sets[i % copies])
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for i in range(reps):
+                fn(sets[(i + 1) % copies])
+            b.record()
+            b.synchronize()
+            return a.elapsed_time(b) * 1e3 / reps
+        t_attn, t_srh, t_naive = timed(attn), timed(srh), timed(naive)
+        res.append({"L": L, "verify_us": round(t_attn, 2), "scoring_heads_us": round(t_srh, 2),
+                    "all_heads_us": round(t_naive, 2), "scoring_heads_vs_verify": round(t_srh / t_attn, 4),
+                    "all_heads_vs_verify": round(t_naive / t_attn, 4)})
+        print(f"[crossover] L={L}: {res[-1]}", file=sys.stderr, flush=True)
+        del sets, ws
+    cross = next((r["L"] for r in res if r["all_heads_us"] > r["verify_us"]), None)
+    print(json.dumps({"metric": "importance estimation cost vs full-cache verification",
+                      "workload_head_shape": cfg.name, "batch": B, "q_heads": Hq, "kv_heads": Hkv, "head_dim": D,
+                      "draft_nodes": N, "scoring_heads": min(SCORE_HEADS, Hkv), "points": res,
+                      "all_heads_first_L_above_verify": cross}), flush=True)
 
 
 def run_steps(torch, ops, cfg, sparse: bool, sets, dev, steps: int, warmup: int):
@@ -567,6 +668,13 @@ def sparse_extras(torch, ops, cfg, sets, r, es):
                 "p10_p90_us": [round(_pct(r["sel_ms"], 10) * 1e3, 2), round(_pct(r["sel_ms"], 90) * 1e3, 2)],
                 "bytes": sel_bytes, "gbs": round(sel_bytes / (sel_avg * 1e-3) / 1e9, 1),
                 "share_of_step": round(sel_avg / r["ms_per_step"], 4)}
+    # Attention Recovery Rate of the first copy's verify set for its own
+    # verification rows (diagnostic: the synthetic scores are unrelated to
+    # q.k, so it sits near the set's share of the cache)
+    arr = ops.attention_recovery(sets[0]["q"], sets[0]["k_cache"], idx_bufs[0])
+    torch.cuda.synchronize()
+    selector["attention_recovery_mean"] = round(float(arr.mean().item()), 4)
+    selector["set_share_of_cache"] = round(n_ctx / cfg.L, 4)
     return gather, selector
 
 
@@ -594,6 +702,9 @@ def main():
     ap.add_argument("--sweep-n", action="store_true",
                     help="instead of the step benchmark: time verification for N = 1..256 draft nodes on the "
                          "workload's cache, calibrate the roofline time model and run the tree-size controller")
+    ap.add_argument("--score-crossover", action="store_true",
+                    help="instead of the step benchmark: importance estimation (a few scoring heads, and every "
+                         "head) against dense verification for L = 2k..32k on the workload's head shape")
     ap.add_argument("--no-read-probe", action="store_true",
                     help="skip the read-only HBM probe (counter-collection runs)")
     ap.add_argument("--copy-calib-gib", type=float, default=0.0,
@@ -606,6 +717,9 @@ def main():
         sys.exit(2)
     if args.sweep_n:
         sweep_n(args)
+        return
+    if args.score_crossover:
+        score_crossover(args)
         return
 
     import torch

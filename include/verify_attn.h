@@ -206,14 +206,29 @@ va_status build_draft_tree(const float* cand_prob, const int32_t* cand_token, in
  * latency and the rule that sizes the draft tree.  Host functions; no GPU
  * work.
  *
- * va_verify_time_model: T_verify(N) = max(bytes(N) / bandwidth,
- * flops(N) / compute) + overhead in seconds for desc's shape with N draft
- * nodes over n_ctx context keys; bytes(N) = 2 B Hkv n_ctx D e (context K/V)
- * + B Hq N D e (queries) + 2 B Hkv N D e (draft K/V) + B Hq N (D e + 4)
- * (output and lse), flops(N) = 4 B Hq N n_ctx D, e = element bytes.  The
- * three constants are calibrated from measured runs (desc->N is ignored). */
-va_status va_verify_time_model(const va_attn_desc* desc, int32_t n_ctx, double bandwidth,
-                               double compute, double overhead, int32_t N, double* seconds);
+ * va_verify_time_model: T_verify(N) in seconds for desc's shape with N draft
+ * nodes over n_ctx context keys, following the plan this library runs (the
+ * pages' model is "calibrated by observed execution times"; its structure
+ * here is the kernels'): with R = (Hq / Hkv) N query rows per KV head cut
+ * into row tiles of `rows` rows (256 in the shared-tile kernel: bf16 with
+ * R > 64; else 32, or 64 for float32 with R > 32) and the context cut into
+ * the call's splits (parts = splits + 1, the tree),
+ *     T = max(KV / bandwidth, Q F_pad / compute_k) + W / bandwidth + overhead
+ * KV = 2 B Hkv n_ctx D e, F_pad = 4 B Hkv tiles rows n_ctx D (padded rows
+ * included), compute_k = compute_shared or compute_tiles by kernel,
+ * Q = ceil(Wg / 256) 256 / Wg for the Wg = B Hkv tiles splits context
+ * workgroups (grid rounds on 256 CUs, one workgroup each), W = 2 B Hq N
+ * parts (D + 1) 4 (partial rows written and merged), e = element bytes.
+ * The constants are effective ones calibrated from measured runs (they
+ * absorb fixed per-call costs); desc->N is ignored. */
+typedef struct {
+  double bandwidth;       /* bytes / s                                          */
+  double compute_shared;  /* flop / s of the shared-tile kernel (padded rows)   */
+  double compute_tiles;   /* flop / s of the per-wavefront kernel (padded rows) */
+  double overhead;        /* seconds per call                                   */
+} va_time_consts;
+va_status va_verify_time_model(const va_attn_desc* desc, int32_t n_ctx, const va_time_consts* consts,
+                               int32_t N, double* seconds);
 
 /* va_choose_tree_size: the tree stops growing when the estimated speedup
  * S(n) = a_hat_cum[n-1] * l_ar / (t_draft + t_verify[n-1]) stops increasing:
@@ -257,6 +272,25 @@ va_status va_scores_workspace_size(const va_score_desc* desc, size_t* bytes);
 va_status importance_scores(const va_score_desc* desc, const void* q, const void* k,
                             float* score, int64_t ld_score,
                             void* ws, size_t ws_bytes, void* stream);
+
+/* Attention Recovery Rate of a verify set (Dustin, "Metodologia" section 2
+ * names it as the objective of the offline choice of scoring heads and of
+ * m; the pages give no formula).  Reading: the share of the full context
+ * attention mass of the verification rows that the set keeps,
+ *     arr[b] = (1 / rows) sum_{k < K} score[b, verify_idx[b, k]]
+ * where score is importance_scores' map over ALL `rows` query rows of the
+ * verification (every query head's draft rows, each against its KV head),
+ * so arr = 1 for the whole cache.  That map may come in pieces (one
+ * importance_scores call takes up to 32 rows of one KV head): with
+ * accumulate != 0 the piece's share is added to arr instead of written.
+ *   score       [B, L] float32 device, row stride ld_score (>= L)
+ *   verify_idx  [B, K] int32 device, row stride idx_stride (>= K), distinct
+ *               indices (duplicates count twice; indices outside [0, L) add 0)
+ *   arr         [B] float32 device, written
+ * One kernel on `stream`; the sum order is fixed (bitwise reproducible). */
+va_status verify_set_recovery(const float* score, int64_t ld_score, int32_t B, int32_t L,
+                              const int32_t* verify_idx, int32_t K, int64_t idx_stride,
+                              int32_t rows, int32_t accumulate, float* arr, void* stream);
 
 /* Accept and commit (Dustin, "Workflow di Verifica" step 5: accepted draft
  * tokens are appended to the cache, rejected ones dropped).  The accepted

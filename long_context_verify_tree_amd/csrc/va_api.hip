@@ -497,6 +497,22 @@ va_status importance_scores(const va_score_desc* desc, const void* q, const void
   return ok();
 }
 
+va_status verify_set_recovery(const float* score, int64_t ld_score, int32_t B, int32_t L, const int32_t* verify_idx,
+                              int32_t K, int64_t idx_stride, int32_t rows, int32_t accumulate, float* arr,
+                              void* stream) {
+  if (B < 0 || L < 0 || K < 0) return fail(VA_EINVAL, "B, L and K must be >= 0");
+  if (rows < 1) return fail(VA_EINVAL, "rows must be >= 1");
+  if (ld_score < L) return fail(VA_EINVAL, "ld_score (%lld) < L (%d)", (long long)ld_score, L);
+  if (K > 0 && idx_stride < K) return fail(VA_EINVAL, "idx_stride (%lld) < K (%d)", (long long)idx_stride, K);
+  if (B == 0) return ok();
+  if (!arr || (K > 0 && (!score || !verify_idx))) return fail(VA_EINVAL, "score, verify_idx and arr must be non-NULL");
+  if (B > 0x7fffffff) return fail(VA_EUNSUPPORTED, "problem too large for one launch");
+  hipError_t e = va::launch_recovery(score, ld_score, B, L, verify_idx, K, idx_stride, rows, accumulate != 0, arr,
+                                     (hipStream_t)stream);
+  if (e != hipSuccess) return fail(VA_EHIP, "recovery kernel launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
 va_status build_draft_tree(const float* cand_prob, const int32_t* cand_token, int32_t B, int32_t K, int32_t T,
                            int32_t N, int32_t* parent, int32_t* token, float* rho, float* a_hat, void* stream) {
   if (B < 0) return fail(VA_EINVAL, "B must be >= 0");
@@ -520,21 +536,29 @@ va_status build_draft_tree(const float* cand_prob, const int32_t* cand_token, in
   return ok();
 }
 
-va_status va_verify_time_model(const va_attn_desc* desc, int32_t n_ctx, double bandwidth, double compute,
-                               double overhead, int32_t N, double* seconds) {
+va_status va_verify_time_model(const va_attn_desc* desc, int32_t n_ctx, const va_time_consts* k, int32_t N,
+                               double* seconds) {
   va_status st = check_desc(desc);
   if (st != VA_OK) return st;
-  if (!seconds) return fail(VA_EINVAL, "seconds is NULL");
-  if (n_ctx < 0 || N < 1) return fail(VA_EINVAL, "n_ctx >= 0 and N >= 1 required");
-  if (!(bandwidth > 0.0) || !(compute > 0.0) || !(overhead >= 0.0))
-    return fail(VA_EINVAL, "bandwidth and compute must be > 0, overhead >= 0");
+  if (!seconds || !k) return fail(VA_EINVAL, "consts and seconds must be non-NULL");
+  if (n_ctx < 0 || N < 1 || N > 256) return fail(VA_EINVAL, "0 <= n_ctx and 1 <= N <= 256 required");
+  if (!(k->bandwidth > 0.0) || !(k->compute_shared > 0.0) || !(k->compute_tiles > 0.0) || !(k->overhead >= 0.0))
+    return fail(VA_EINVAL, "bandwidth and compute rates must be > 0, overhead >= 0");
+  va_attn_desc d = *desc;
+  d.N = N;
+  const va::Plan pl = make_plan(&d, n_ctx);
   const double e = desc->dtype == VA_BF16 ? 2.0 : 4.0;
-  const double B = desc->B, Hq = desc->Hq, Hkv = desc->Hkv, D = desc->D, L = n_ctx, n = N;
-  const double bytes = 2.0 * B * Hkv * L * D * e + B * Hq * n * D * e + 2.0 * B * Hkv * n * D * e +
-                       B * Hq * n * D * e + B * Hq * n * 4.0;
-  const double flops = 4.0 * B * Hq * n * L * D;
-  const double tb = bytes / bandwidth, tf = flops / compute;
-  *seconds = (tb > tf ? tb : tf) + overhead;
+  const double B = desc->B, Hq = desc->Hq, Hkv = desc->Hkv, D = desc->D, L = n_ctx;
+  const double rows = pl.rb == va::kRowsKernel ? 256.0 : 32.0 * pl.rb;
+  const double kv = 2.0 * B * Hkv * L * D * e;
+  const double f_pad = 4.0 * B * Hkv * pl.row_tiles * rows * L * D;
+  const double w = 2.0 * B * Hq * N * pl.n_parts * (D + 1) * 4.0;
+  const double comp = pl.rb == va::kRowsKernel ? k->compute_shared : k->compute_tiles;
+  // grid rounds of one context workgroup per CU of the plan's 256-CU target
+  const double groups = (double)desc->B * desc->Hkv * pl.row_tiles * pl.n_ctx_splits;
+  const double q = groups > 0 ? ceil(groups / VA_TARGET_GROUPS) * VA_TARGET_GROUPS / groups : 1.0;
+  const double tb = kv / k->bandwidth, tf = q * f_pad / comp;
+  *seconds = (tb > tf ? tb : tf) + w / k->bandwidth + k->overhead;
   return ok();
 }
 

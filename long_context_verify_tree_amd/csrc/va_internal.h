@@ -106,6 +106,8 @@ struct TreeParams {
 // the hipError_t of the launch.
 hipError_t launch_tree(const TreeParams& p, hipStream_t stream);
 hipError_t launch_scores(const ScoreParams& p, int D, hipStream_t stream);
+hipError_t launch_recovery(const float* score, int64_t ld, int B, int L, const int32_t* idx, int K,
+                           int64_t idx_stride, int rows, int accumulate, float* arr, hipStream_t stream);
 hipError_t launch_commit(const CommitParams& p, hipStream_t stream);
 hipError_t launch_partials(const PartialParams& p, int dtype, int D, int rb, bool gather,
                            hipStream_t stream);

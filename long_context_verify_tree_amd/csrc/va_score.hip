@@ -198,7 +198,40 @@ __global__ __launch_bounds__(256) void score_finish_kernel(ScoreParams p) {
     if (j + e < p.L) out[j + e] = acc[e];
 }
 
+// Attention Recovery Rate of a verify set (Dustin, "Metodologia" section
+// 2): the share of the importance map of all verification rows that falls
+// on the set, arr[b] (+)= sum_k score[b, idx[b, k]] / rows.  One workgroup per
+// sequence; each thread sums a fixed strided subset of the set, then a fixed
+// reduction tree (bitwise reproducible).  Indices outside [0, L) add 0.
+__global__ __launch_bounds__(256) void recovery_kernel(const float* score, int64_t ld, int L, const int32_t* idx,
+                                                       int K, int64_t idx_stride, float inv_rows, int accumulate,
+                                                       float* arr) {
+  __shared__ float part[256];
+  const int b = blockIdx.x;
+  const float* srow = score + (int64_t)b * ld;
+  const int32_t* irow = idx + (int64_t)b * idx_stride;
+  float acc = 0.f;
+  for (int k = threadIdx.x; k < K; k += 256) {
+    const int j = irow[k];
+    acc += (unsigned)j < (unsigned)L ? srow[j] : 0.f;
+  }
+  part[threadIdx.x] = acc;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if ((int)threadIdx.x < w) part[threadIdx.x] += part[threadIdx.x + w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) arr[b] = (accumulate ? arr[b] : 0.f) + part[0] * inv_rows;
+}
+
 }  // namespace
+
+hipError_t launch_recovery(const float* score, int64_t ld, int B, int L, const int32_t* idx, int K,
+                           int64_t idx_stride, int rows, int accumulate, float* arr, hipStream_t stream) {
+  hipLaunchKernelGGL(recovery_kernel, dim3(B), dim3(256), 0, stream, score, ld, L, idx, K, idx_stride,
+                     1.0f / (float)rows, accumulate, arr);
+  return hipGetLastError();
+}
 
 hipError_t launch_scores(const ScoreParams& p, int D, hipStream_t stream) {
   if (D == 64)

@@ -64,9 +64,10 @@ def _declare(lib):
         "accept_commit": (i32, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
         "va_scores_workspace_size": (i32, [_P, _P]),
         "build_draft_tree": (i32, [_P, _P, i32, i32, i32, i32, _P, _P, _P, _P, _P]),
-        "va_verify_time_model": (i32, [_P, i32, ctypes.c_double, ctypes.c_double, ctypes.c_double, i32, _P]),
+        "va_verify_time_model": (i32, [_P, i32, _P, i32, _P]),
         "va_choose_tree_size": (i32, [_P, _P, i32, ctypes.c_double, ctypes.c_double, _P]),
         "importance_scores": (i32, [_P, _P, _P, _P, i64, _P, sz, _P]),
+        "verify_set_recovery": (i32, [_P, i64, i32, i32, _P, i32, i64, i32, i32, _P, _P]),
         "va_status_str": (ctypes.c_char_p, [i32]),
         "va_last_error": (ctypes.c_char_p, []),
         "va_version": (i32, []),
@@ -334,6 +335,50 @@ def importance_scores(q, k, scale: Optional[float] = None, out=None, workspace=N
     return out
 
 
+def verify_set_recovery(score, verify_idx, rows: int, out=None, accumulate: bool = False) -> torch.Tensor:
+    """Attention Recovery Rate [B] float32 of the verify sets verify_idx
+    [B, K] from (a piece of) the importance map score [B, L] of all `rows`
+    verification query rows; accumulate adds the piece's share to out."""
+    load()
+    if score.dtype != torch.float32 or score.dim() != 2 or score.stride(1) != 1:
+        raise ValueError("score must be float32 [B, L] with contiguous rows")
+    if verify_idx.dtype != torch.int32 or verify_idx.dim() != 2 or \
+            (verify_idx.shape[1] > 1 and verify_idx.stride(1) != 1):
+        raise ValueError("verify_idx must be int32 [B, K] with unit column stride")
+    B, L = score.shape
+    K = verify_idx.shape[1]
+    if out is None:
+        if accumulate:
+            raise ValueError("accumulate needs out")
+        out = torch.empty(B, dtype=torch.float32, device=score.device)
+    _check(_lib.verify_set_recovery(_ptr(score), _row_stride(score, L), B, L, _ptr(verify_idx), K,
+                                    _row_stride(verify_idx, K) if K else 0, rows, int(accumulate), _ptr(out),
+                                    _stream(score.device)))
+    return out
+
+
+def attention_recovery(q, k_cache, verify_idx, workspace=None) -> torch.Tensor:
+    """Attention Recovery Rate [B] of verify_idx for the verification rows q
+    [B, Hq, N, D] over k_cache [B, Hkv, L, D]: importance_scores over every
+    query row (the G query heads of a KV head are its G * N rows, taken 32 at
+    a time), each piece's share accumulated by verify_set_recovery."""
+    B, Hq, N, D = q.shape
+    Hkv = k_cache.shape[1]
+    G = Hq // Hkv
+    L = k_cache.shape[2]
+    rows = q.reshape(B, Hkv, G * N, D)
+    score = torch.empty(B, L, dtype=torch.float32, device=q.device)
+    arr = torch.empty(B, dtype=torch.float32, device=q.device)
+    first = True
+    for kvh in range(Hkv):
+        for r0 in range(0, G * N, 32):
+            importance_scores(rows[:, kvh:kvh + 1, r0:r0 + 32], k_cache[:, kvh:kvh + 1], out=score,
+                              workspace=workspace)
+            verify_set_recovery(score, verify_idx, Hq * N, out=arr, accumulate=not first)
+            first = False
+    return arr
+
+
 def make_commit_desc(k_cache, v_cache, k_draft, v_draft) -> AttnDesc:
     """Descriptor for accept_commit: caches [B, Hkv, capacity, D], drafts
     [B, Hkv, N, D] (desc.L = capacity; query/output fields unused)."""
@@ -406,11 +451,19 @@ def build_draft_tree(cand_prob, cand_token, N: int):
     return parent, token, rho, a_hat
 
 
-def verify_time_model(desc: AttnDesc, n_ctx: int, bandwidth: float, compute: float, overhead: float, N: int) -> float:
-    """Roofline estimate of the verification time (seconds) of N draft nodes."""
+class TimeConsts(ctypes.Structure):
+    _fields_ = [("bandwidth", ctypes.c_double), ("compute_shared", ctypes.c_double),
+                ("compute_tiles", ctypes.c_double), ("overhead", ctypes.c_double)]
+
+
+def verify_time_model(desc: AttnDesc, n_ctx: int, bandwidth: float, compute_shared: float, compute_tiles: float,
+                      overhead: float, N: int) -> float:
+    """Estimated verification time (seconds) of N draft nodes, following the
+    library's kernel plan, with calibrated constants."""
     load()
+    k = TimeConsts(bandwidth, compute_shared, compute_tiles, overhead)
     out = ctypes.c_double()
-    _check(_lib.va_verify_time_model(ctypes.byref(desc), n_ctx, bandwidth, compute, overhead, N, ctypes.byref(out)))
+    _check(_lib.va_verify_time_model(ctypes.byref(desc), n_ctx, ctypes.byref(k), N, ctypes.byref(out)))
     return out.value
 
 

@@ -348,6 +348,39 @@ def importance_scores(q: np.ndarray, k: np.ndarray, scale: Optional[float] = Non
     return out
 
 
+def attention_recovery(q: np.ndarray, k_cache: np.ndarray, verify_idx: np.ndarray,
+                       scale: Optional[float] = None) -> np.ndarray:
+    """Attention Recovery Rate of a verify set per sequence (Dustin,
+    "Metodologia" section 2 names it as the objective of the offline choice
+    of scoring heads; the pages give no formula).  Plain reading: the share
+    of the full attention mass that the verify set keeps, i.e. for sequence
+    b the mean over query heads h and draft rows i of
+
+        sum_{j in I_verify[b]} softmax_j(scale * <q[b,h,i], k_cache[b, h // G, j]>)
+
+    with the softmax over the L context keys (the draft keys are never
+    dropped, so they are not part of it).  q [B, Hq, N, D], k_cache
+    [B, Hkv, L, D], verify_idx [B, K] (a set: duplicates count once).
+    Returns float64 [B]; an empty set recovers 0."""
+    qf, kf = as_f64(q), as_f64(k_cache)
+    B, Hq, N, D = qf.shape
+    Hkv = kf.shape[1]
+    G = Hq // Hkv
+    sc = default_scale(D) if scale is None or scale <= 0 else float(scale)
+    out = np.zeros(B, dtype=np.float64)
+    for b in range(B):
+        sel = np.unique(np.asarray(verify_idx[b], dtype=np.int64))
+        total = 0.0
+        for h in range(Hq):
+            s = sc * (qf[b, h] @ kf[b, h // G].T)            # [N, L]
+            s = s - s.max(axis=1, keepdims=True)
+            p = np.exp(s)
+            p = p / p.sum(axis=1, keepdims=True)
+            total += p[:, sel].sum()
+        out[b] = total / (Hq * N)
+    return out
+
+
 # ---------------------------------------------------------------------------
 # best-first draft tree
 
@@ -421,6 +454,59 @@ def verify_time_model(B: int, Hq: int, Hkv: int, D: int, n_ctx: int, N: int, ele
     """Roofline estimate of T_verify(N) in seconds with calibrated constants."""
     nbytes, flops = verify_bytes_flops(B, Hq, Hkv, D, n_ctx, N, elem_bytes)
     return max(nbytes / bandwidth, flops / compute) + overhead
+
+
+def kernel_plan(B: int, Hq: int, Hkv: int, n_ctx: int, N: int, elem_bytes: int):
+    """How the verification library cuts one call into work (its documented
+    plan, restated here): the G * N query rows of a KV head go in row tiles
+    of 256 rows (the shared-tile kernel, bf16 with more than 64 rows), else
+    32 rows (bf16), else 32 or 64 rows (fp32, 64 when more than 32 rows);
+    the context keys go in splits sized for about one context workgroup per
+    CU of a 256-CU device (splits of a multiple of 128 keys, at least 512),
+    and the tree is one more part.  Returns (shared_tile_kernel, rows per
+    tile, row tiles per KV head, context splits, parts)."""
+    R = (Hq // Hkv) * N
+    shared = elem_bytes == 2 and R > 64
+    if shared:
+        rows = 256
+    elif elem_bytes == 2 or R <= 32:
+        rows = 32
+    else:
+        rows = 64
+    tiles = -(-R // rows)
+    pairs = B * Hkv * tiles
+    want = max(1, -(-256 // pairs))
+    split = -(-n_ctx // want) if n_ctx > 0 else 128
+    split = max(512, -(-split // 128) * 128)
+    splits = -(-n_ctx // split) if n_ctx > 0 else 0
+    return shared, rows, tiles, splits, splits + 1
+
+
+def verify_time_plan(B: int, Hq: int, Hkv: int, D: int, n_ctx: int, N: int, elem_bytes: int,
+                     bandwidth: float, compute_shared: float, compute_tiles: float, overhead: float) -> float:
+    """T_verify(N) following the kernel plan (BASTION's latency model,
+    calibrated on measured runs, with the structure of the kernels that run):
+
+        T = max(KV / bandwidth, Q * F_pad / compute_k) + W / bandwidth + overhead
+
+    KV = 2 B Hkv n_ctx D e (the context rows, read once); F_pad = 4 B Hkv
+    tiles rows n_ctx D (the MFMA work of every row of every row tile, padding
+    included); compute_k = compute_shared for the shared-tile kernel, else
+    compute_tiles; Q = ceil(Wg / 256) * 256 / Wg, the rounds in which the
+    Wg = B Hkv tiles splits context workgroups run on 256 CUs (one workgroup
+    per CU) over the rounds a perfectly divided grid would need; W =
+    2 B Hq N parts (D + 1) 4 (the float32 partial rows and their
+    log-sum-exps, written by the partial kernel and read by the merge).  The
+    constants are effective ones: the fit lets them absorb what the terms
+    leave out (fixed per-call costs, L2 reuse)."""
+    shared, rows, tiles, splits, parts = kernel_plan(B, Hq, Hkv, n_ctx, N, elem_bytes)
+    kv = 2.0 * B * Hkv * n_ctx * D * elem_bytes
+    f_pad = 4.0 * B * Hkv * tiles * rows * n_ctx * D
+    groups = B * Hkv * tiles * splits
+    q = (-(-groups // 256)) * 256.0 / groups if groups > 0 else 1.0
+    w = 2.0 * B * Hq * N * parts * (D + 1) * 4
+    comp = compute_shared if shared else compute_tiles
+    return max(kv / bandwidth, q * f_pad / comp) + w / bandwidth + overhead
 
 
 def choose_tree_size(a_hat_cum: Sequence[float], t_verify: Sequence[float], t_draft: float, l_ar: float):

@@ -229,14 +229,26 @@ def test_tree_rejects_before_launch(ops):
 def test_controller_host_functions_match_the_oracle(ops):
     # host functions of the library: no GPU involved
     from oracle import verify_oracle as vo
-    d = good_desc(ops, B=8, Hq=32, Hkv=8, D=128, L=32768, N=8)
     rng = np.random.default_rng(3)
-    for _ in range(20):
-        bw, fl, c0 = rng.uniform(1e12, 8e12), rng.uniform(1e14, 2.5e15), rng.uniform(0, 1e-5)
-        n_ctx, N = int(rng.integers(0, 1 << 17)), int(rng.integers(1, 257))
-        got = ops.verify_time_model(d, n_ctx, bw, fl, c0, N)
-        want = vo.verify_time_model(8, 32, 8, 128, n_ctx, N, 2, bw, fl, c0)
-        assert got == pytest.approx(want, rel=1e-12)
+    for shape in (dict(B=8, Hq=32, Hkv=8, D=128, L=32768), dict(B=4, Hq=64, Hkv=8, D=128, L=131072),
+                  dict(B=16, Hq=28, Hkv=4, D=128, L=32768), dict(B=1, Hq=4, Hkv=1, D=64, L=256, dtype=0),
+                  dict(B=2, Hq=8, Hkv=1, D=64, L=5000, dtype=0)):
+        d = good_desc(ops, N=8, **shape)
+        e = 4 if shape.get("dtype", 1) == 0 else 2
+        for _ in range(40):
+            bw, cs, ct, c0 = rng.uniform(1e12, 8e12), rng.uniform(5e14, 2.5e15), rng.uniform(1e14, 1e15), \
+                rng.uniform(0, 1e-5)
+            n_ctx, N = int(rng.integers(0, shape["L"] + 1)), int(rng.integers(1, 257))
+            got = ops.verify_time_model(d, n_ctx, bw, cs, ct, c0, N)
+            want = vo.verify_time_plan(shape["B"], shape["Hq"], shape["Hkv"], shape["D"], n_ctx, N, e, bw, cs, ct, c0)
+            assert got == pytest.approx(want, rel=1e-12), (shape, n_ctx, N)
+            # and the parts of that plan are the library's (its workspace size)
+            d.N = N
+            _, ws = ws_size(ops, d, n_ctx)
+            rows = shape["B"] * shape["Hq"] * N
+            parts = vo.kernel_plan(shape["B"], shape["Hq"], shape["Hkv"], n_ctx, N, e)[4]
+            assert ws == -(-rows * parts * shape["D"] * 4 // 256) * 256 + -(-rows * parts * 4 // 256) * 256
+            d.N = 8
     for _ in range(50):
         n = int(rng.integers(1, 40))
         a = np.cumsum(rng.random(n) ** 2).astype(np.float32)
@@ -244,6 +256,6 @@ def test_controller_host_functions_match_the_oracle(ops):
         t_draft, l_ar = float(rng.uniform(0, 1e-4)), float(rng.uniform(1e-4, 2e-4))
         assert ops.choose_tree_size(a, t, t_draft, l_ar) == vo.choose_tree_size(a, t, t_draft, l_ar)[0]
     with pytest.raises(ops.VerifyAttnError):
-        ops.verify_time_model(d, 100, 0.0, 1e15, 0.0, 4)
+        ops.verify_time_model(d, 100, 0.0, 1e15, 1e15, 0.0, 4)
     with pytest.raises(ops.VerifyAttnError):
         ops.choose_tree_size(np.ones(3), np.ones(3), 0.0, 0.0)

@@ -78,3 +78,29 @@ def test_scores_full_size_qwen_sparse_workload(gpu_lib):
     got = _gpu(gpu_lib, q, k)
     ref = vo.importance_scores(q, k)
     np.testing.assert_allclose(got, ref, rtol=1e-4, atol=1e-9)
+
+
+@pytest.mark.parametrize("shape", [
+    dict(B=2, Hq=28, Hkv=4, N=8, D=128, L=3000),     # Qwen2.5-7B head shape: 56 rows per KV head (2 pieces)
+    dict(B=1, Hq=64, Hkv=8, N=20, D=128, L=1500),    # 70B head shape: 160 rows per KV head (5 pieces)
+    dict(B=2, Hq=4, Hkv=1, N=5, D=64, L=700),        # D = 64, one piece
+])
+def test_attention_recovery_matches_the_oracle(gpu_lib, shape):
+    ops = gpu_lib
+    rng = np.random.default_rng(shape["L"])
+    B, Hq, Hkv, N, D, L = (shape[k] for k in ("B", "Hq", "Hkv", "N", "D", "L"))
+    q = synth.f32_to_bf16_bits(rng.standard_normal((B, Hq, N, D)).astype(np.float32) * 2.0)
+    kc = synth.f32_to_bf16_bits(rng.standard_normal((B, Hkv, L, D)).astype(np.float32))
+    qd, kd = to_dev(q, synth.BF16), to_dev(kc, synth.BF16)
+    for K in (L // 7, L // 2):
+        idx = np.sort(np.stack([rng.permutation(L)[:K] for _ in range(B)]), axis=1).astype(np.int32)
+        print(f"case recovery {shape} K={K}", flush=True)
+        got = ops.attention_recovery(qd, kd, torch.from_numpy(idx).cuda())
+        torch.cuda.synchronize()
+        want = vo.attention_recovery(q, kc, idx)
+        np.testing.assert_allclose(got.cpu().numpy(), want, rtol=1e-4, atol=1e-6)
+    print(f"case recovery {shape} whole cache / empty set", flush=True)
+    all_idx = torch.arange(L, dtype=torch.int32).repeat(B, 1).cuda()
+    np.testing.assert_allclose(ops.attention_recovery(qd, kd, all_idx).cpu().numpy(), 1.0, rtol=1e-4)
+    empty = torch.zeros(B, 0, dtype=torch.int32).cuda()
+    np.testing.assert_array_equal(ops.attention_recovery(qd, kd, empty).cpu().numpy(), 0.0)

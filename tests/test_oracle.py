@@ -638,6 +638,41 @@ def test_scores_bf16_bits_and_default_scale():
                                rtol=1e-14)
 
 
+def test_attention_recovery_pins():
+    rng = np.random.default_rng(31)
+    B, Hq, Hkv, N, D, L = 2, 4, 2, 3, 16, 40
+    q = rng.standard_normal((B, Hq, N, D))
+    kc = rng.standard_normal((B, Hkv, L, D))
+    # the whole cache recovers everything, the empty set nothing
+    np.testing.assert_allclose(vo.attention_recovery(q, kc, np.tile(np.arange(L), (B, 1))), 1.0, rtol=1e-14)
+    np.testing.assert_array_equal(vo.attention_recovery(q, kc, np.zeros((B, 0), dtype=np.int64)), 0.0)
+    # equal keys: every key carries 1 / L of every row's mass
+    flat = np.tile(rng.standard_normal(D), (B, Hkv, L, 1))
+    idx = np.stack([rng.permutation(L)[:13] for _ in range(B)])
+    np.testing.assert_allclose(vo.attention_recovery(q, flat, idx), 13 / L, rtol=1e-13)
+    # complementary sets add up to 1; duplicates count once
+    perm = rng.permutation(L)
+    a = vo.attention_recovery(q, kc, np.tile(perm[:17], (B, 1)))
+    c = vo.attention_recovery(q, kc, np.tile(perm[17:], (B, 1)))
+    np.testing.assert_allclose(a + c, 1.0, rtol=1e-13)
+    np.testing.assert_allclose(vo.attention_recovery(q, kc, np.tile(np.r_[perm[:17], perm[:5]], (B, 1))), a,
+                               rtol=1e-14)
+    # a dominant key: one key equal to a large multiple of a row's query
+    # takes almost all of that row's mass (two-key logistic closed form)
+    q1 = np.zeros((1, 1, 1, 2)); q1[0, 0, 0] = [1.0, 0.0]
+    k1 = np.array([[[[3.0, 0.0], [0.0, 1.0]]]])
+    sc = 1 / np.sqrt(2)
+    want = 1 / (1 + np.exp(-3.0 * sc))
+    np.testing.assert_allclose(vo.attention_recovery(q1, k1, np.array([[0]])), want, rtol=1e-14)
+    # equals the importance map of all the verification rows gathered on the
+    # set, divided by the rows (the map is the oracle's own sum of probabilities)
+    for b in range(B):
+        per_kv = [vo.importance_scores(q[b:b + 1, kvh * 2:(kvh + 1) * 2].reshape(1, 1, 2 * N, D),
+                                       kc[b:b + 1, kvh:kvh + 1]) for kvh in range(Hkv)]
+        score = sum(per_kv)[0]
+        np.testing.assert_allclose(score[idx[b]].sum() / (Hq * N), vo.attention_recovery(q, kc, idx)[b], rtol=1e-12)
+
+
 # ---------------------------------------------------------------------------
 # best-first draft tree (BASTION, "Surrogato di Accettazione ed Espansione
 # Best-First": best-first expansion maximises the summed path scores)
@@ -803,6 +838,67 @@ def test_time_model_regimes_and_ridge():
     knee = next(n for n in range(1, 257)
                 if vo.verify_bytes_flops(N=n, **args)[1] / fl > vo.verify_bytes_flops(N=n, **args)[0] / bw)
     assert knee == math.ceil(fl / bw * 8 / 32)
+
+
+def test_kernel_plan_hand_cases():
+    # Llama-3-8B layer shape (G = 4), batch 8, 32768 keys, bf16: worked by hand
+    # from the plan rules.  N = 8: 32 rows, one 32-row tile, 64 (b, kvh)
+    # pairs -> 4 splits of 8192 keys
+    assert vo.kernel_plan(8, 32, 8, 32768, 8, 2) == (False, 32, 1, 4, 5)
+    # N = 16: 64 rows, still the per-wavefront kernel, two 32-row tiles ->
+    # 128 pairs -> 2 splits of 16384
+    assert vo.kernel_plan(8, 32, 8, 32768, 16, 2) == (False, 32, 2, 2, 3)
+    # N = 17: 68 rows -> the shared-tile kernel, one 256-row tile
+    assert vo.kernel_plan(8, 32, 8, 32768, 17, 2) == (True, 256, 1, 4, 5)
+    # N = 65: 260 rows -> two 256-row tiles -> 128 pairs -> 2 splits
+    assert vo.kernel_plan(8, 32, 8, 32768, 65, 2) == (True, 256, 2, 2, 3)
+    # 70B shape (G = 8), batch 4, 131072 keys, N = 128: 1024 rows, 4 tiles,
+    # 128 pairs -> 2 splits of 65536
+    assert vo.kernel_plan(4, 64, 8, 131072, 128, 2) == (True, 256, 4, 2, 3)
+    # short context: splits never below 512 keys; no context: only the tree part
+    assert vo.kernel_plan(1, 4, 1, 700, 8, 2) == (False, 32, 1, 2, 3)
+    assert vo.kernel_plan(1, 4, 1, 0, 8, 2) == (False, 32, 1, 0, 1)
+    # fp32: 32-row tiles up to 32 rows, 64-row tiles above
+    assert vo.kernel_plan(1, 4, 1, 256, 8, 4)[1:3] == (32, 1)
+    assert vo.kernel_plan(1, 8, 1, 256, 7, 4)[1:3] == (64, 1)
+    assert vo.kernel_plan(1, 8, 1, 256, 9, 4)[1:3] == (64, 2)
+
+
+def test_plan_time_model_closed_forms():
+    args = dict(B=8, Hq=32, Hkv=8, D=128, n_ctx=32768, elem_bytes=2)
+    bw, cs, ct, c0 = 5e12, 1.2e15, 0.4e15, 4e-6
+    kv = 2 * 8 * 8 * 32768 * 128 * 2
+    # N = 8: memory-bound per-wavefront kernel, 5 parts
+    w8 = 2 * 8 * 32 * 8 * 5 * 129 * 4
+    assert vo.verify_time_plan(N=8, bandwidth=bw, compute_shared=cs, compute_tiles=ct, overhead=c0, **args) == \
+        pytest.approx(kv / bw + w8 / bw + c0, rel=1e-12)
+    # N = 64: one 256-row tile of the shared-tile kernel (256 rows, no
+    # padding): compute 4 * 8 * 8 * 256 * 32768 * 128 flops at cs
+    f = 4 * 8 * 8 * 256 * 32768 * 128
+    w64 = 2 * 8 * 32 * 64 * 5 * 129 * 4
+    assert vo.verify_time_plan(N=64, bandwidth=bw, compute_shared=cs, compute_tiles=ct, overhead=c0, **args) == \
+        pytest.approx(max(kv / bw, f / cs) + w64 / bw + c0, rel=1e-12)
+    # N = 33 and N = 64 run the same padded work (one 256-row tile): they
+    # differ only in the partial rows
+    t33 = vo.verify_time_plan(N=33, bandwidth=bw, compute_shared=cs, compute_tiles=ct, overhead=0.0, **args)
+    t64 = vo.verify_time_plan(N=64, bandwidth=bw, compute_shared=cs, compute_tiles=ct, overhead=0.0, **args)
+    assert t64 - t33 == pytest.approx(2 * 8 * 32 * (64 - 33) * 5 * 129 * 4 / bw, rel=1e-9)
+    # one more node past a tile boundary adds a whole tile of padded work
+    t65 = vo.verify_time_plan(N=65, bandwidth=bw, compute_shared=cs, compute_tiles=ct, overhead=0.0, **args)
+    assert t65 - t64 == pytest.approx((f / cs) * (2 - 1) - 2 * 8 * 32 * 64 * 5 * 129 * 4 / bw
+                                      + 2 * 8 * 32 * 65 * 3 * 129 * 4 / bw, rel=1e-9)
+    # grid rounds: 70B shape, 4 sequences.  N = 96: 768 rows -> 3 tiles, 96
+    # (b, kvh, tile) pairs -> 3 splits -> 288 context workgroups, 2 rounds of
+    # 256 where 1.125 would do: the compute term is 512 / 288 of the padded
+    # work's; N = 128: 4 tiles, 2 splits, 256 workgroups, one round.
+    a70 = dict(B=4, Hq=64, Hkv=8, D=128, n_ctx=131072, elem_bytes=2)
+    big_c = dict(bandwidth=1e30, compute_shared=1e15, compute_tiles=1e15, overhead=0.0)
+    f96 = 4 * 4 * 8 * 3 * 256 * 131072 * 128
+    w96 = 2 * 4 * 64 * 96 * 4 * 129 * 4
+    assert vo.verify_time_plan(N=96, **a70, **big_c) == pytest.approx(512 / 288 * f96 / 1e15 + w96 / 1e30, rel=1e-12)
+    f128 = 4 * 4 * 8 * 4 * 256 * 131072 * 128
+    assert vo.verify_time_plan(N=128, **a70, **big_c) == pytest.approx(f128 / 1e15, rel=1e-12)
+    assert vo.verify_time_plan(N=128, **a70, **big_c) < vo.verify_time_plan(N=96, **a70, **big_c)
 
 
 def test_controller_stops_at_the_first_decrease():
