@@ -33,7 +33,7 @@ def test_verify_mode_and_names():
 def test_selector_kernel_choice():
     # one 32768-token segment: the single-workgroup kernel
     assert bench.select_kernel_name(16, 32768, 2048) == "select_kernel"
-    # longer rows whose 8192-token workgroups all fit at once: several workgroups per row
+    # longer rows whose 16384-token workgroups all fit at once: several workgroups per row
     assert bench.select_kernel_name(4, 131072, 4096) == "select_cluster_kernel"
     assert bench.select_kernel_name(32, 131072, 4096) == "select_cluster_kernel"    # 32 * 8 = 256 groups
     assert bench.select_kernel_name(33, 131072, 4096) == "select_kernel"            # 264 > 256
