@@ -52,9 +52,8 @@ def algorithmic(cfg, n_ctx: int, sparse: bool):
 
 
 CSRC = os.path.join(ROOT, "long_context_verify_tree_amd", "csrc")
-KERNEL_SOURCES = {"partial_kernel": "va_attn.hip", "rows_kernel": "va_attn.hip", "select_kernel": "va_select.hip",
-                  "select_cluster_kernel": "va_select.hip", "score_partial_kernel": "va_score.hip"}
-SELECT_SEG_TOKENS, SELECT_CLUSTER_TOKENS, SELECT_CLUSTER_MAX_GROUPS = 32768, 16384, 256
+KERNEL_SOURCES = {"partial_kernel": "va_attn.hip", "rows_kernel": "va_attn.hip", "select_filter_kernel": "va_select.hip",
+                  "select_resolve_kernel": "va_select.hip", "score_partial_kernel": "va_score.hip"}
 
 
 def committed_summary(kernel: str, workload: str, suffix: str = ""):
@@ -104,13 +103,10 @@ def attention_kernel(cfg) -> str:
 
 
 def select_kernel_name(B: int, L: int, budget: int) -> str:
-    """Which selector kernel the library runs: rows longer than one 32768-token
-    segment go to the multi-workgroup kernel when all its workgroups
-    (16384 tokens each) fit on the device at once."""
-    parts = -(-L // SELECT_CLUSTER_TOKENS)
-    if budget < L and L > SELECT_SEG_TOKENS and B * parts <= SELECT_CLUSTER_MAX_GROUPS:
-        return "select_cluster_kernel"
-    return "select_kernel"
+    """The selector's kernels: a filter over many workgroups per row, then one
+    resolving workgroup per row; with budget >= L only the second runs (every
+    index is taken)."""
+    return "select_filter_kernel+select_resolve_kernel" if budget < L else "select_resolve_kernel"
 
 
 def verify_mode(cfg, verify: str) -> bool:

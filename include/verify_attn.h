@@ -319,10 +319,10 @@ va_status accept_commit(const va_attn_desc* desc, void* k_cache, void* v_cache,
                         const int32_t* accepted, const int32_t* cache_len, int32_t* new_len,
                         void* stream);
 
-/* Workspace bytes needed by select_verify_set for B rows of L scores
- * (zero when each row runs in one workgroup; rows longer than 32768 tokens
- * of a small batch are split over several workgroups that meet through the
- * workspace).  Calls that overlap in time must not share a workspace. */
+/* Workspace bytes needed by select_verify_set for B rows of L scores when
+ * it selects (budget < L): per row, about 6 bytes per token for the
+ * candidate lists its first kernel writes and its second reads.  Calls that
+ * overlap in time must not share a workspace. */
 va_status va_select_workspace_size(int32_t B, int32_t L, size_t* bytes);
 
 /* Verify-set selection.
@@ -330,18 +330,17 @@ va_status va_select_workspace_size(int32_t B, int32_t L, size_t* bytes);
  *   sink, window, top_m >= 0; budget >= min(L, |[0,sink) U [L-window,L)|)
  *   verify_idx  [B, min(budget, L)] int32, contiguous; ascending, distinct
  *   ws          device workspace of va_select_workspace_size(B, L) bytes
+ *               (unused, and may be NULL, when budget >= L)
  * budget >= L returns every index 0..L-1.  With budget < L, rows longer
- * than 786432 tokens (24 x 32768) return VA_EUNSUPPORTED: each row's token
- * marks are kept on chip.
- * Rows longer than 32768 tokens of a batch whose 16384-token workgroups
- * (B * ceil(L / 16384) of them, at most 256) the device holds at once (by
- * the occupancy API) are split over several workgroups that wait for one
- * another; other batches take one workgroup per row.  Every such wait is
- * bounded, since work on other streams can hold CUs: should one time out,
- * that row of verify_idx is filled with -1 (never a
- * valid index; verify_attn_sparse stays memory-safe on it, with an
- * unspecified result), so a row whose first entry is -1 must not be used
- * as a verify set. */
+ * than 786432 tokens (24 x 32768) return VA_EUNSUPPORTED: a row whose
+ * sample misses is resolved by one workgroup that re-reads the row on
+ * every radix pass, and the limit bounds that time.
+ * Two kernels run on `stream`: a filter over 4096-token workgroups that
+ * lists, per row, every token either tier could take (key bounds from a
+ * row-wide sample), then one workgroup per row that finds both thresholds
+ * exactly among the listed tokens (or over the whole row when the list
+ * cannot hold them) and writes the verify set.  Neither waits on another
+ * workgroup. */
 va_status select_verify_set(const float* draft_score, const float* target_score,
                             int32_t B, int32_t L, int64_t ld,
                             int32_t sink, int32_t window, int32_t top_m, int32_t budget,

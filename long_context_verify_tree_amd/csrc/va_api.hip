@@ -347,7 +347,7 @@ va_status select_verify_set(const float* draft_score, const float* target_score,
     return fail(VA_EUNSUPPORTED, "L = %d exceeds the selector limit of %d tokens", L, va::kSelectMaxL);
   if (budget < L && (!draft_score || !target_score))
     return fail(VA_EINVAL, "draft_score and target_score must be non-NULL");
-  const size_t need = va::select_ws_bytes(B, L);
+  const size_t need = budget < L ? va::select_ws_bytes(B, L) : 0;
   if (need > 0 && (ws == nullptr || ws_bytes < need))
     return fail(VA_EWORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws ? ws_bytes : (size_t)0);
   hipError_t e = va::launch_select(draft_score, target_score, B, L, ld, sink, window, top_m, budget, verify_idx, ws,

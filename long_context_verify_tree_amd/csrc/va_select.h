@@ -8,9 +8,10 @@
 
 namespace va {
 
-// Longest score row the selector handles.  The kernel keeps one mark word
-// per thread and 32768-token segment in LDS (4 KiB per segment) beside about
-// 48 KiB of histograms; 24 segments keep the total within a CU's 160 KiB.
+// Longest score row the selector handles.  A row whose candidate list
+// cannot be resolved from the filter's output is resolved by one workgroup
+// that re-reads the row in 32768-token segments on every radix pass; the
+// limit bounds that time.
 constexpr int32_t kSelectSegTokens = 32768;
 constexpr int32_t kSelectMaxL = 24 * kSelectSegTokens;
 

@@ -3,53 +3,64 @@
 // window, take the top-m tokens by draft-lookahead score, then fill the rest
 // of the budget with the best remaining tokens by target-historical score.
 //
-// One workgroup of 1024 threads per sequence.  The row is cut into segments
-// of 32768 tokens; in each segment thread t owns the 32 consecutive tokens
-// 32t .. 32t+31, so "lower index first" is thread order and then bit order,
-// and one 32-bit word per thread and segment holds the thread's selection
-// marks.  Each tier is an exact top-r over the candidates (tokens between
-// sink and window, minus those already taken):
-//   * scores become order-preserving 32-bit keys (NaN lowest, -0 == +0);
-//   * three radix passes (12, 10 and 10 bits) over LDS histograms (integer
-//     atomics, so counts do not depend on thread order) find the key T of the
-//     r-th best candidate and the number of candidates strictly above it.
-//     The first pass of both tiers shares one sweep: the target histogram
-//     counts every free token, and the draft tier's picks are subtracted
-//     from it before the target tier starts;
-//   * one block-wide exclusive scan of each thread's count of keys equal to
-//     T gives every such token its rank in index order; the first ones up to
-//     r are taken (the lower-index tie rule).
-// A last block scan of the per-thread mark counts (plus sink and window)
-// writes the ascending index list.  A row of one segment keeps its keys in
-// registers for all passes; longer rows re-read each segment per pass (the
-// row then sits in L2).  Rows longer than one segment go to a second kernel
-// instead (select_cluster_kernel, below) when the batch is small enough:
-// several workgroups per row, each holding 16384 tokens in registers.
+// Each tier is an exact top-r over its candidates (the free tokens between
+// sink and window; for the target tier, minus the draft tier's picks), ties
+// going to the lower index.  Scores become order-preserving 32-bit keys (NaN
+// lowest, -0 == +0) and a token's rank is the 64-bit value (key << 32) |
+// ~index: higher is better, and no two tokens share one.  A tier's result is
+// one threshold P, the rank of its r-th best candidate; the tier takes
+// exactly the candidates whose rank is >= P.
+//
+// Two kernels per call, with no waits between workgroups:
+//   * select_filter_kernel, many 4096-token workgroups per row.  Every
+//     workgroup of a row reads the same row-wide sample (one 32-token run per
+//     block of the row, at most 128 blocks) and derives from it, for each
+//     tier, a key bound K below which the tier surely does not reach: the
+//     top-12-bit bucket of sample rank r f + 4 sqrt(r f) + 4 (f the sample's
+//     share of the free tokens; for the target tier the sample leaves out
+//     the tokens at or above the draft bound, a superset of the draft picks,
+//     which can only lower K).  It then writes, in index order, every free
+//     token of its segment with a draft key >= K_d or a target key >= K_t
+//     (both keys and the index) to its own region of the workspace.
+//   * select_resolve_kernel, one 1024-thread workgroup per row, gathers the
+//     regions into LDS, still in index order.  If the draft tier has at least
+//     r1 listed candidates and the target tier (listed tokens below the draft
+//     threshold with a target key >= K_t) at least r2, every token a tier
+//     could take is listed, and each threshold is found among the listed
+//     entries alone: radix passes (12, 10 and 10 bits) of LDS histograms
+//     until the bin of the r-th best holds at most 64 entries, whose ranks
+//     are then compared with one another, or, after the last pass, an
+//     index-order scan of the entries equal to the threshold key.  The
+//     output (sink, the listed entries at or above their tier's threshold,
+//     window) follows from one scan of the list.  Otherwise (a sample far
+//     off, a full region or list) the same workgroup takes the exact way
+//     over the whole row: the same radix passes over every key, re-read from
+//     the row per pass, and an index-order scan of the threshold key's ties.
 
 #include <stdint.h>
 #include <stdlib.h>
 
-#include <atomic>
-
 #include <hip/hip_runtime.h>
 
+#include "va_device.h"
 #include "va_select.h"
 
 namespace va {
 namespace {
 
-constexpr int kST = 1024;                 // threads per workgroup
-constexpr int kSWaves = kST / 64;
-constexpr int kKPT = 32;                  // tokens per thread per segment
-constexpr int kSeg = kST * kKPT;          // tokens per segment
-static_assert(kSeg == kSelectSegTokens, "segment size of the length limit");
+constexpr int kBins = 4096;               // buckets of a key's top 12 bits
+constexpr int kTiny = 64;                 // entries of the last bin compared pairwise
+constexpr uint64_t kNone = ~0ull;         // threshold that takes no token
+constexpr uint32_t kNoKey = 0xFFFFFFFFu;  // key bound that lists no token (keys are <= 0xFF800000)
 
 struct SelParams {
   const float* ds;
   const float* ts;
   int32_t* out;
   int64_t ld;
-  int L, sink, window, top_m, budget, k_out;
+  int L, budget, k_out;
+  int lo, hi, n_free, r1, r2;   // free tokens [lo, hi); picks of the two tiers
+  int exact;                    // take the exact way only (a test hook)
 };
 
 __device__ inline uint32_t order_key(float f) {
@@ -59,9 +70,10 @@ __device__ inline uint32_t order_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Exclusive prefix sum of v over the workgroup in thread order; *total gets
-// the sum.  Uses wsum[kSWaves]; two barriers, or one with TAIL = false when
-// the caller reaches another barrier before wsum is written again.
+__device__ inline uint32_t key_of_bits(uint32_t bits) { return order_key(__uint_as_float(bits)); }
+
+__device__ inline uint64_t rank_of(uint32_t key, int j) { return ((uint64_t)key << 32) | (uint32_t)~(uint32_t)j; }
+
 // Inclusive prefix sum over the 64 lanes of a wavefront with DPP moves (no
 // LDS round trip): shifts by 1, 2, 4, 8 within each row of 16 lanes (lanes
 // without a source read 0), then lane 15 of rows 0 and 2 is added to rows 1
@@ -76,7 +88,10 @@ __device__ inline int wave_incl_scan(int x) {
   return x;
 }
 
-template <bool TAIL = true, int NW = kSWaves>
+// Exclusive prefix sum of v over the workgroup (NW wavefronts) in thread
+// order; *total gets the sum.  One barrier, plus a second with TAIL for a
+// caller that writes wsum again before its next barrier.
+template <bool TAIL, int NW>
 __device__ inline int block_excl_scan(int v, int* wsum, int* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int x = wave_incl_scan(v);
@@ -94,545 +109,596 @@ __device__ inline int block_excl_scan(int v, int* wsum, int* total) {
   return before + x - v;
 }
 
-// Radix digits of a 32-bit key: 12 bits, then 10, then 10.
-constexpr int kDigitBits[3] = {12, 10, 10};
-constexpr int kDigitShift[3] = {20, 10, 0};
-constexpr int kBins0 = 1 << 12;
-
-struct SelShared {
-  int hist_d[kBins0];        // first-digit histogram of the draft tier
-  int hist_t[kBins0];        // first-digit histogram of the target tier
-  int hist_p[2][2][1 << 10]; // [tier][pass - 1]: later digits, zeroed with the others at the start
-  int wsum[kSWaves];
-  int pick[2];               // digit, candidates in higher buckets
-};
-
-// Bits of the 32 tokens [j0, j0 + 32) that lie in [lo, hi).
-__device__ inline uint32_t range_bits(int j0, int lo, int hi) {
-  const int a = lo - j0, e = hi - j0;   // bit i set for a <= i < e
-  const uint32_t below_e = e <= 0 ? 0u : (e >= 32 ? ~0u : (1u << e) - 1u);
-  const uint32_t below_a = a <= 0 ? 0u : (a >= 32 ? ~0u : (1u << a) - 1u);
-  return below_e & ~below_a;
+// Bits of the four tokens [b, b + 4) that lie in [lo, hi).
+__device__ inline uint32_t nib_bits(int b, int lo, int hi) {
+  int a = lo - b, e = hi - b;
+  a = a < 0 ? 0 : (a > 4 ? 4 : a);
+  e = e < 0 ? 0 : (e > 4 ? 4 : e);
+  return ((1u << e) - 1u) & ~((1u << a) - 1u);
 }
 
-// Given a histogram of `nbins` buckets (nbins / kST per thread, highest
-// buckets at the lowest threads) and `above` candidates in higher buckets
-// already, finds the bucket holding the r-th largest candidate: sets
-// sh.pick = {bucket, candidates above it}.  Two barriers; every thread
-// reads the result after the last, which also orders the next use of wsum.
-__device__ inline void pick_bucket(const int* hist, int nbins, int r, int above, SelShared& sh) {
-  const int tid = threadIdx.x;
-  const int per = nbins / kST;   // 4 or 1
-  const int top = nbins - per * tid;   // this thread's buckets: [top - per, top)
-  int c[4] = {0, 0, 0, 0};
+// Counts of a histogram of NB buckets split over NT threads (NB / NT each,
+// the highest buckets at the lowest threads): c[] gets this thread's counts,
+// highest first; returns the count in higher buckets and *total the sum.
+// One barrier; the caller reaches another before wsum is written again.
+template <int NT, int NB>
+__device__ inline int bins_scan(const int* hist, int (&c)[NB / NT], int* wsum, int* total) {
+  constexpr int PER = NB / NT;
+  const int top = NB - PER * (int)threadIdx.x;
   int csum = 0;
-  for (int k = 0; k < per; ++k) {
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
     c[k] = hist[top - 1 - k];
     csum += c[k];
   }
-  int tot;
-  int cum = above + block_excl_scan<false>(csum, sh.wsum, &tot);
-  if (cum < r && cum + csum >= r) {
-    int bucket = top - 1;
-    for (int k = 0; k < per; ++k) {
-      if (cum + c[k] >= r) {
-        bucket = top - 1 - k;
-        break;
-      }
-      cum += c[k];
-    }
-    sh.pick[0] = bucket;
-    sh.pick[1] = cum;
-  }
-  __syncthreads();
+  return block_excl_scan<false, NT / 64>(csum, wsum, total);
 }
 
-static_assert(sizeof(SelShared) + (size_t)(kSelectMaxL / kSeg) * kST * sizeof(uint32_t) <= 160 * 1024,
-              "histograms and the mark words of the longest row must fit in LDS");
+// If the rank-th largest entry (1-based) lies in this thread's buckets
+// (cum entries in higher ones), returns its bucket and sets *above to the
+// entries in higher buckets; else -1.
+template <int NT, int NB>
+__device__ inline int bins_find(const int (&c)[NB / NT], int cum, int rank, int* above) {
+  constexpr int PER = NB / NT;
+  const int top = NB - PER * (int)threadIdx.x;
+  if (rank <= cum) return -1;
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    if (rank <= cum + c[k]) {
+      *above = cum;
+      return top - 1 - k;
+    }
+    cum += c[k];
+  }
+  return -1;
+}
 
-template <bool RESIDENT>
-__global__ __launch_bounds__(kST) void select_kernel(SelParams p) {
-  extern __shared__ uint32_t marks[];   // [nseg][kST]: tokens taken by the two tiers
-  __shared__ SelShared sh;
+// Radix digits of a key: 12 bits, then 10, then 10.
+__device__ inline int digit_shift(int pass) { return pass == 0 ? 20 : (pass == 1 ? 10 : 0); }
+__device__ inline int digit_bins(int pass) { return pass == 0 ? kBins : 1024; }
+
+// ---------------------------------------------------------------------------
+// The filter: 512 threads, 8 tokens each (two runs of four), per 4096-token
+// segment.  Thread t holds tokens base + 2048 q + 4 t + e (q < 2, e < 4) as
+// bit 4 q + e, so each load of four tokens is coalesced across the
+// wavefront and index order is (q, t, e).
+
+constexpr int kFT = 512;                   // threads per filter workgroup
+constexpr int kFW = kFT / 64;
+constexpr int kFSeg = 8 * kFT;             // tokens per filter workgroup
+constexpr int kFCap = kFSeg / 2;           // entries a segment may list
+constexpr int kSampBlocks = 128;           // row-wide sample: at most this many 32-token runs
+constexpr int kSampPT = kSampBlocks * 32 / kFT;   // sample tokens per thread (8)
+constexpr int kMaxFP = (kSelectMaxL + kFSeg - 1) / kFSeg;   // segments of the longest row
+static_assert(kSampPT == 8, "two runs of four sample tokens per thread");
+
+// Workspace of one row, in ints: the two key bounds, the segments' list
+// counts, then per segment its listed draft keys, target keys and indices.
+constexpr int kWsKd = 0;
+constexpr int kWsKt = 1;
+constexpr int kWsCnt = 64;
+constexpr int kWsReg = kWsCnt + (kMaxFP + 63) / 64 * 64;
+constexpr int kRegInts = 3 * kFCap;
+
+__host__ __device__ inline int filter_parts(int L) { return (L + kFSeg - 1) / kFSeg; }
+__host__ __device__ inline int64_t row_ints(int L) { return kWsReg + (int64_t)filter_parts(L) * kRegInts; }
+
+struct FShared {
+  int hs[kBins];
+  int wsum[kFW];
+  int pick;
+};
+
+// Key bound of a tier from the sample histogram sh.hs: the bucket holding
+// sample rank ceil(r f + 4 sqrt(r f) + 4), f = S / n_free (S < 0: the
+// histogram's own total), shifted to a key; 0 when the sample holds fewer.
+// *total gets the histogram's total.  Two barriers.
+__device__ inline uint32_t key_bound(int r, int S, int n_free, FShared& sh, int* total) {
+  int c[kBins / kFT], tot;
+  if (threadIdx.x == 0) sh.pick = 0;
+  const int cum = bins_scan<kFT, kBins>(sh.hs, c, sh.wsum, &tot);
+  const float fe = (float)r * (float)(S < 0 ? tot : S) / (float)n_free;
+  const int rank = (int)ceilf(fe + 4.0f * sqrtf(fe) + 4.0f);
+  int ab;
+  const int bk = bins_find<kFT, kBins>(c, cum, rank, &ab);
+  if (bk >= 0) sh.pick = bk;
+  __syncthreads();
+  *total = tot;
+  return (uint32_t)sh.pick << 20;
+}
+
+__global__ __launch_bounds__(kFT) void select_filter_kernel(SelParams p, int* ws_all, int P) {
+  __shared__ FShared sh;
+  const int tid = threadIdx.x;
+  const int b = blockIdx.x / P, seg = blockIdx.x % P;
+  const int base = seg * kFSeg;
+  int* ws = ws_all + (int64_t)b * row_ints(p.L);
+  const float* ds = p.ds + (int64_t)b * p.ld;
+  const float* ts = p.ts + (int64_t)b * p.ld;
+  const int L = p.L, lo = p.lo, hi = p.hi;
+
+  // this segment's scores (raw bits first, so that every load is in flight
+  // at once), then the row-wide sample: block k of nblk (each sb tokens)
+  // contributes the 32-token run at 32 * (7 k mod sb / 32) past its start;
+  // this thread takes tokens u .. u + 3 of the runs for u = 4 t, 4 t + 2048
+  uint32_t kd[8], kt[8];
+  const int b0 = base + 4 * tid;
+  const bool aligned = ((reinterpret_cast<uintptr_t>(ds) | reinterpret_cast<uintptr_t>(ts)) & 15u) == 0;
+  const dev::rsrc_t rsd = dev::make_rsrc(ds, (uint32_t)L * 4u), rst = dev::make_rsrc(ts, (uint32_t)L * 4u);
+  if (aligned && base + kFSeg <= L) {
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const uint4 a = *reinterpret_cast<const uint4*>(ds + b0 + q * 4 * kFT);
+      const uint4 c = *reinterpret_cast<const uint4*>(ts + b0 + q * 4 * kFT);
+      kd[4 * q + 0] = a.x, kd[4 * q + 1] = a.y, kd[4 * q + 2] = a.z, kd[4 * q + 3] = a.w;
+      kt[4 * q + 0] = c.x, kt[4 * q + 1] = c.y, kt[4 * q + 2] = c.z, kt[4 * q + 3] = c.w;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int j = b0 + (i >> 2) * 4 * kFT + (i & 3);   // (past L: reads 0, never listed)
+      kd[i] = __builtin_amdgcn_raw_buffer_load_b32(rsd, j * 4, 0, 0);
+      kt[i] = __builtin_amdgcn_raw_buffer_load_b32(rst, j * 4, 0, 0);
+    }
+  }
+  const int nblk0 = (L + 255) / 256;
+  const int nblk = nblk0 < kSampBlocks ? nblk0 : kSampBlocks;
+  const int sb = (L + 32 * nblk - 1) / (32 * nblk) * 32;
+  uint32_t sd[kSampPT], st[kSampPT];
+  int sj[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int u = 4 * tid + h * 4 * kFT;
+    const int k = u >> 5;
+    const int j = k * sb + 32 * ((7 * k) % (sb / 32)) + (u & 31);
+    sj[h] = k < nblk ? j : L;
+    if (aligned && k < nblk && j + 4 <= L) {
+      const uint4 a = *reinterpret_cast<const uint4*>(ds + j);
+      const uint4 c = *reinterpret_cast<const uint4*>(ts + j);
+      sd[4 * h + 0] = a.x, sd[4 * h + 1] = a.y, sd[4 * h + 2] = a.z, sd[4 * h + 3] = a.w;
+      st[4 * h + 0] = c.x, st[4 * h + 1] = c.y, st[4 * h + 2] = c.z, st[4 * h + 3] = c.w;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        sd[4 * h + e] = __builtin_amdgcn_raw_buffer_load_b32(rsd, (sj[h] + e) * 4, 0, 0);
+        st[4 * h + e] = __builtin_amdgcn_raw_buffer_load_b32(rst, (sj[h] + e) * 4, 0, 0);
+      }
+    }
+  }
+  for (int i = tid; i < kBins; i += kFT) sh.hs[i] = 0;
+  uint32_t sfree = 0;   // sample tokens that are free
+#pragma unroll
+  for (int k = 0; k < kSampPT; ++k) {
+    const int j = sj[k >> 2] + (k & 3);
+    sfree |= (uint32_t)(j >= lo && j < hi) << k;
+    sd[k] = key_of_bits(sd[k]);
+  }
+  __syncthreads();
+
+  // the key bounds of the two tiers
+  uint32_t K_d = kNoKey, K_t = kNoKey;
+  int S = 0;   // free sample tokens
+  if (p.r1 > 0) {
+#pragma unroll
+    for (int k = 0; k < kSampPT; ++k)
+      if ((sfree >> k) & 1u) atomicAdd(&sh.hs[sd[k] >> 20], 1);
+    __syncthreads();
+    K_d = key_bound(p.r1, -1, p.n_free, sh, &S);
+    for (int i = tid; i < kBins; i += kFT) sh.hs[i] = 0;
+    __syncthreads();
+  } else {
+    block_excl_scan<true, kFW>(__popc(sfree), sh.wsum, &S);
+  }
+  if (p.r2 > 0) {
+#pragma unroll
+    for (int k = 0; k < kSampPT; ++k)
+      if (((sfree >> k) & 1u) && sd[k] < K_d) atomicAdd(&sh.hs[key_of_bits(st[k]) >> 20], 1);
+    __syncthreads();
+    int t2;
+    K_t = key_bound(p.r2, S, p.n_free, sh, &t2);
+  }
+  if (seg == 0 && tid == 0) {
+    ws[kWsKd] = (int)K_d;
+    ws[kWsKt] = (int)K_t;
+  }
+
+  // list, in index order, the free tokens either tier could take
+  uint32_t keep = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    kd[i] = key_of_bits(kd[i]);
+    kt[i] = key_of_bits(kt[i]);
+    const int j = b0 + (i >> 2) * 4 * kFT + (i & 3);
+    keep |= (uint32_t)(j >= lo && j < hi && (kd[i] >= K_d || kt[i] >= K_t)) << i;
+  }
+  const int v = __popc(keep & 15u) | (__popc(keep >> 4) << 16);
+  int tot;
+  const int ex = block_excl_scan<false, kFW>(v, sh.wsum, &tot);
+  const int n0 = tot & 0xffff, n = n0 + (tot >> 16);
+  int* reg = ws + kWsReg + (int64_t)seg * kRegInts;
+  int pos0 = ex & 0xffff, pos1 = n0 + (ex >> 16);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    if ((keep >> i) & 1u) {
+      const int at = i < 4 ? pos0++ : pos1++;
+      if (at < kFCap) {
+        reg[at] = (int)kd[i];
+        reg[kFCap + at] = (int)kt[i];
+        reg[2 * kFCap + at] = b0 + (i >> 2) * 4 * kFT + (i & 3);
+      }
+    }
+  }
+  if (tid == 0) ws[kWsCnt + seg] = n;
+}
+
+// ---------------------------------------------------------------------------
+// The resolve: one workgroup of 1024 threads per row.
+
+constexpr int kRT = 1024;                  // threads per resolve workgroup
+constexpr int kRW = kRT / 64;
+constexpr int kRCap = 8192;                // list entries resolved in LDS
+constexpr int kEPT = kRCap / kRT;          // list entries per thread at most (8)
+constexpr int kSeg = kRT * 32;             // tokens per exact-way segment
+static_assert(kSeg == kSelectSegTokens, "segment size of the length limit");
+static_assert(kMaxFP <= kRT, "one segment count per thread");
+
+struct RShared {
+  union {
+    struct {
+      uint32_t kd[kRCap];
+      uint32_t kt[kRCap];
+      int j[kRCap];
+    } e;                      // the row's list, in index order
+    int off[kMaxFP];          // (segment offsets, before the list is read)
+  } u;
+  int h0[kBins];              // top 12 bits
+  int h1[1024];               // a later digit
+  uint64_t tiny[kTiny];
+  int wsum[kRW];
+  int pick[2];
+  int ntiny;
+  uint64_t pstar;
+};
+
+// Threshold of the r-th best among the list entries of this thread's span
+// [e0, e0 + cnt) whose bit is set in cand (bit e - e0), by key (the kd or kt
+// list).  Radix passes until the r-th best's bin holds at most kTiny
+// entries (then compared pairwise), else an index-order scan of its ties
+// after the last pass.
+__device__ __forceinline__ uint64_t list_select(const uint32_t* key, const int* jj, int e0, int cnt, uint32_t cand, int r,
+                                RShared& sh) {
+  const int tid = threadIdx.x;
+  uint32_t prefix = 0, fixed = 0;   // key bits found so far, and their mask
+  int above = 0;
+  for (int pass = 0; pass < 3; ++pass) {
+    const int shift = digit_shift(pass), nb = digit_bins(pass);
+    int* hist = pass == 0 ? sh.h0 : sh.h1;
+    for (int i = tid; i < nb; i += kRT) hist[i] = 0;
+    if (tid == 0) sh.ntiny = 0;
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < kEPT; ++k) {
+      if (k < cnt && ((cand >> k) & 1u)) {
+        const uint32_t kv = key[e0 + k];
+        if ((kv & fixed) == prefix) atomicAdd(&hist[(kv >> shift) & (uint32_t)(nb - 1)], 1);
+      }
+    }
+    __syncthreads();
+    int bk = -1, ab = 0;
+    if (pass == 0) {
+      int c[kBins / kRT], t;
+      const int cum = above + bins_scan<kRT, kBins>(hist, c, sh.wsum, &t);
+      bk = bins_find<kRT, kBins>(c, cum, r, &ab);
+    } else {
+      int c[1024 / kRT], t;
+      const int cum = above + bins_scan<kRT, 1024>(hist, c, sh.wsum, &t);
+      bk = bins_find<kRT, 1024>(c, cum, r, &ab);
+    }
+    if (bk >= 0) {
+      sh.pick[0] = bk;
+      sh.pick[1] = ab;
+    }
+    __syncthreads();
+    prefix |= (uint32_t)sh.pick[0] << shift;
+    fixed |= (uint32_t)(nb - 1) << shift;
+    above = sh.pick[1];
+    const int E = hist[sh.pick[0] & (nb - 1)];
+    if (E <= kTiny) {
+      // the bin's entries, compared pairwise
+#pragma unroll
+      for (int k = 0; k < kEPT; ++k) {
+        if (k < cnt && ((cand >> k) & 1u)) {
+          const uint32_t kv = key[e0 + k];
+          if ((kv & fixed) == prefix) {
+            const int s = atomicAdd(&sh.ntiny, 1);
+            if (s < kTiny) sh.tiny[s] = rank_of(kv, jj[e0 + k]);
+          }
+        }
+      }
+      __syncthreads();
+      if (tid < E) {
+        const uint64_t rv = sh.tiny[tid];
+        int rk = 0;
+        for (int x = 0; x < E; ++x) rk += sh.tiny[x] > rv;
+        if (rk == r - above - 1) sh.pstar = rv;
+      }
+      __syncthreads();
+      return sh.pstar;
+    }
+    __syncthreads();   // (every thread has read the bin's count)
+  }
+  // more than kTiny entries share the key T = prefix: the (r - above)-th of
+  // them in list (index) order is the last taken
+  int eq = 0;
+#pragma unroll
+  for (int k = 0; k < kEPT; ++k) eq += (k < cnt && ((cand >> k) & 1u) && key[e0 + k] == prefix) ? 1 : 0;
+  int tot;
+  int before = block_excl_scan<true, kRW>(eq, sh.wsum, &tot);
+  const int need = r - above;
+#pragma unroll
+  for (int k = 0; k < kEPT; ++k) {
+    if (k < cnt && ((cand >> k) & 1u) && key[e0 + k] == prefix) {
+      if (++before == need) sh.pstar = rank_of(prefix, jj[e0 + k]);
+    }
+  }
+  __syncthreads();
+  return sh.pstar;
+}
+
+// The exact way.  A segment of 32768 tokens: thread t holds tokens
+// base + 4096 q + 4 t + e (q < 8, e < 4) as bit 4 q + e; index order is
+// (q, t, e).  Tokens past L read 0 (never candidates).
+__device__ inline void seg_keys(dev::rsrc_t rs, bool vec, const float* row, int base, uint32_t (&key)[32]) {
+  const int b0 = base + 4 * (int)threadIdx.x;
+  if (vec) {
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const uint4 v = *reinterpret_cast<const uint4*>(row + b0 + q * 4 * kRT);
+      key[4 * q + 0] = v.x, key[4 * q + 1] = v.y, key[4 * q + 2] = v.z, key[4 * q + 3] = v.w;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 32; ++i)
+      key[i] = __builtin_amdgcn_raw_buffer_load_b32(rs, (b0 + (i >> 2) * 4 * kRT + (i & 3)) * 4, 0, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < 32; ++i) key[i] = key_of_bits(key[i]);
+}
+
+__device__ inline int seg_token(int base, int i) { return base + (i >> 2) * 4 * kRT + 4 * (int)threadIdx.x + (i & 3); }
+
+__device__ inline uint32_t seg_bits(int base, int lo, int hi) {
+  const int b0 = base + 4 * (int)threadIdx.x;
+  uint32_t m = 0;
+#pragma unroll
+  for (int q = 0; q < 8; ++q) m |= nib_bits(b0 + q * 4 * kRT, lo, hi) << (4 * q);
+  return m;
+}
+
+// Bits of this thread's tokens whose rank is >= P.
+__device__ inline uint32_t seg_sel(const uint32_t (&key)[32], int base, uint64_t P) {
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) m |= (uint32_t)(rank_of(key[i], seg_token(base, i)) >= P) << i;
+  return m;
+}
+
+// The exact way for one tier over the whole row: threshold of the r-th best
+// candidate by the keys of `row` (for the target tier, the draft picks, rank
+// >= pd by the keys of drow, are not candidates).
+__device__ uint64_t exact_tier(const SelParams p, const float* row, const float* drow, uint64_t pd, bool target,
+                               int r, RShared& sh) {
+  const int tid = threadIdx.x;
+  const int L = p.L, nseg = (L + kSeg - 1) / kSeg;
+  const dev::rsrc_t rs = dev::make_rsrc(row, (uint32_t)L * 4u), rsd = dev::make_rsrc(drow, (uint32_t)L * 4u);
+  const bool al = ((reinterpret_cast<uintptr_t>(row) | reinterpret_cast<uintptr_t>(drow)) & 15u) == 0;
+  uint32_t key[32];
+  auto cand_of = [&](int s) __attribute__((always_inline)) {
+    uint32_t c = seg_bits(s * kSeg, p.lo, p.hi);
+    if (target) {
+      uint32_t k2[32];
+      seg_keys(rsd, al && (s + 1) * kSeg <= L, drow, s * kSeg, k2);
+      c &= ~seg_sel(k2, s * kSeg, pd);
+    }
+    return c;
+  };
+  uint32_t prefix = 0, fixed = 0;
+  int above = 0;
+  for (int pass = 0; pass < 3; ++pass) {
+    const int shift = digit_shift(pass), nb = digit_bins(pass);
+    int* hist = pass == 0 ? sh.h0 : sh.h1;
+    for (int i = tid; i < nb; i += kRT) hist[i] = 0;
+    __syncthreads();
+    for (int s = 0; s < nseg; ++s) {
+      const uint32_t cand = cand_of(s);
+      seg_keys(rs, al && (s + 1) * kSeg <= L, row, s * kSeg, key);
+#pragma unroll
+      for (int i = 0; i < 32; ++i)
+        if (((cand >> i) & 1u) && (key[i] & fixed) == prefix)
+          atomicAdd(&hist[(key[i] >> shift) & (uint32_t)(nb - 1)], 1);
+    }
+    __syncthreads();
+    int bk = -1, ab = 0;
+    if (pass == 0) {
+      int c[kBins / kRT], t;
+      const int cum = above + bins_scan<kRT, kBins>(hist, c, sh.wsum, &t);
+      bk = bins_find<kRT, kBins>(c, cum, r, &ab);
+    } else {
+      int c[1024 / kRT], t;
+      const int cum = above + bins_scan<kRT, 1024>(hist, c, sh.wsum, &t);
+      bk = bins_find<kRT, 1024>(c, cum, r, &ab);
+    }
+    if (bk >= 0) {
+      sh.pick[0] = bk;
+      sh.pick[1] = ab;
+    }
+    __syncthreads();
+    prefix |= (uint32_t)sh.pick[0] << shift;
+    fixed |= (uint32_t)(nb - 1) << shift;
+    above = sh.pick[1];
+    __syncthreads();   // (every thread has read the pick)
+  }
+  // the (r - above)-th candidate equal to T in index order is the last taken
+  const int need = r - above;
+  int run = 0;
+  for (int s = 0; s < nseg; ++s) {
+    const uint32_t cand = cand_of(s);
+    seg_keys(rs, al && (s + 1) * kSeg <= L, row, s * kSeg, key);
+    uint32_t eq = 0;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) eq |= (uint32_t)(((cand >> i) & 1u) && key[i] == prefix) << i;
+    for (int q = 0; q < 8; ++q) {   // one scan per run of 4096 tokens
+      const uint32_t nbits = (eq >> (4 * q)) & 15u;
+      int tot;
+      int before = run + block_excl_scan<true, kRW>(__popc(nbits), sh.wsum, &tot);
+      for (int e = 0; e < 4; ++e) {
+        if ((nbits >> e) & 1u) {
+          if (++before == need) sh.pstar = rank_of(prefix, seg_token(s * kSeg, 4 * q + e));
+        }
+      }
+      run += tot;
+    }
+  }
+  __syncthreads();
+  return sh.pstar;
+}
+
+// Output of the exact way: sink, the tiers' picks and window, ascending.
+__device__ void exact_output(const SelParams p, const float* ds, const float* ts, int32_t* out, uint64_t pd,
+                             uint64_t pt, RShared& sh) {
+  const int L = p.L, nseg = (L + kSeg - 1) / kSeg;
+  const dev::rsrc_t rsd = dev::make_rsrc(ds, (uint32_t)L * 4u), rst = dev::make_rsrc(ts, (uint32_t)L * 4u);
+  const bool al = ((reinterpret_cast<uintptr_t>(ds) | reinterpret_cast<uintptr_t>(ts)) & 15u) == 0;
+  int written = 0;
+  for (int s = 0; s < nseg; ++s) {
+    uint32_t key[32];
+    const bool vec = al && (s + 1) * kSeg <= L;
+    const uint32_t f = seg_bits(s * kSeg, p.lo, p.hi), valid = seg_bits(s * kSeg, 0, L);
+    seg_keys(rsd, vec, ds, s * kSeg, key);
+    const uint32_t dsel = f & seg_sel(key, s * kSeg, pd);
+    seg_keys(rst, vec, ts, s * kSeg, key);
+    const uint32_t sel = (valid & ~f) | dsel | (f & ~dsel & seg_sel(key, s * kSeg, pt));
+    for (int q = 0; q < 8; ++q) {
+      const uint32_t nbits = (sel >> (4 * q)) & 15u;
+      int tot;
+      int pos = written + block_excl_scan<true, kRW>(__popc(nbits), sh.wsum, &tot);
+      for (int e = 0; e < 4; ++e) {
+        if ((nbits >> e) & 1u) {
+          if (pos < p.k_out) out[pos] = seg_token(s * kSeg, 4 * q + e);
+          ++pos;
+        }
+      }
+      written += tot;
+    }
+  }
+}
+
+__global__ __launch_bounds__(kRT) void select_resolve_kernel(SelParams p, const int* ws_all, int P) {
+  __shared__ RShared sh;
   const int tid = threadIdx.x;
   const int b = blockIdx.x;
   const float* ds = p.ds + (int64_t)b * p.ld;
   const float* ts = p.ts + (int64_t)b * p.ld;
   int32_t* out = p.out + (int64_t)b * p.k_out;
-  const int L = p.L;
+  const int L = p.L, lo = p.lo, hi = p.hi, r1 = p.r1, r2 = p.r2;
   if (p.budget >= L) {
-    for (int j = tid; j < L; j += kST) out[j] = j;
+    for (int j = tid; j < L; j += kRT) out[j] = j;
     return;
   }
-  const int lo = p.sink < L ? p.sink : L;
-  const int w = p.window < L ? p.window : L;
-  const int hi = L - w > lo ? L - w : lo;
-  const int n_prot = lo + (L - hi);
-  const int rest = p.budget - n_prot;
-  const int n_free = hi - lo;
-  int r1 = p.top_m < rest ? p.top_m : rest;
-  r1 = r1 < n_free ? r1 : n_free;
-  const int r2 = rest - r1;
-  const int nseg = RESIDENT ? 1 : (L + kSeg - 1) / kSeg;
-
-  for (int s = 0; s < nseg; ++s) marks[s * kST + tid] = 0u;
-  for (int i = tid; i < kBins0; i += kST) {
-    sh.hist_d[i] = 0;
-    sh.hist_t[i] = 0;
-    (&sh.hist_p[0][0][0])[i] = 0;
-  }
-
-  uint32_t kd[kKPT], kt[kKPT];
-  auto load_keys = [&](const float* row, int s, uint32_t (&key)[kKPT]) __attribute__((always_inline)) {
-    const int j0 = s * kSeg + tid * kKPT;
-    const bool vec = j0 + kKPT <= L && ((reinterpret_cast<uintptr_t>(row + j0) & 15u) == 0);
-    if (vec) {
-#pragma unroll
-      for (int q = 0; q < kKPT / 4; ++q) {
-        const float4 v = *reinterpret_cast<const float4*>(row + j0 + 4 * q);
-        key[4 * q + 0] = order_key(v.x);
-        key[4 * q + 1] = order_key(v.y);
-        key[4 * q + 2] = order_key(v.z);
-        key[4 * q + 3] = order_key(v.w);
+  uint64_t pd = kNone, pt = kNone;
+  if (!p.exact) {
+    const int* ws = ws_all + (int64_t)b * row_ints(L);
+    // segment offsets of the list (a count past kFCap marks a full region)
+    const int c = tid < P ? ws[kWsCnt + tid] : 0;
+    int tot;
+    const int off = block_excl_scan<true, kRW>(c + (c > kFCap ? (1 << 20) : 0), sh.wsum, &tot);
+    const int n = tot & ((1 << 20) - 1);
+    bool ok = (tot >> 20) == 0 && n <= kRCap;
+    if (ok) {
+      // gather the regions into LDS in index order, G threads per region
+      if (tid < P) sh.u.off[tid] = off;
+      __syncthreads();
+      const int G = kRT / P;
+      const int s = tid / G, lt = tid % G;
+      int so = 0, sc = 0;
+      if (s < P) {
+        so = sh.u.off[s];
+        sc = (s + 1 < P ? sh.u.off[s + 1] : n) - so;
       }
-    } else {
-#pragma unroll
-      for (int i = 0; i < kKPT; ++i) key[i] = j0 + i < L ? order_key(row[j0 + i]) : 0u;
-    }
-  };
-  auto free_bits = [&](int s) __attribute__((always_inline)) -> uint32_t {
-    return range_bits(s * kSeg + tid * kKPT, lo, hi);
-  };
-
-  // first digit of both tiers in one sweep; the target histogram counts
-  // every free token and is corrected for the draft tier's picks later
-  if (RESIDENT) {
-    load_keys(ds, 0, kd);
-    load_keys(ts, 0, kt);
-  }
-  __syncthreads();
-  for (int s = 0; s < nseg; ++s) {
-    if (!RESIDENT) {
-      load_keys(ds, s, kd);
-      load_keys(ts, s, kt);
-    }
-    const uint32_t cand = free_bits(s);
-#pragma unroll
-    for (int i = 0; i < kKPT; ++i) {
-      if ((cand >> i) & 1u) {
-        if (r1 > 0) atomicAdd(&sh.hist_d[kd[i] >> kDigitShift[0]], 1);
-        if (r2 > 0) atomicAdd(&sh.hist_t[kt[i] >> kDigitShift[0]], 1);
-      }
-    }
-  }
-  __syncthreads();
-
-  // Marks the top r candidates (free tokens not yet marked) of a tier whose
-  // first-digit histogram is hist0; key holds the keys when resident.
-  auto tier = [&](const float* row, int r, int* hist0, int (&histp)[2][1 << 10], uint32_t (&key)[kKPT])
-                  __attribute__((always_inline)) {
-    uint32_t prefix = 0;
-    int above = 0;
-    pick_bucket(hist0, kBins0, r, 0, sh);
-    prefix = (uint32_t)sh.pick[0] << kDigitShift[0];
-    above = sh.pick[1];
-    for (int pass = 1; pass < 3; ++pass) {
-      const int shift = kDigitShift[pass];
-      const int nb = 1 << kDigitBits[pass];
-      const int hs = shift + kDigitBits[pass];   // bits above this digit are fixed
-      int* hist = histp[pass - 1];               // zeroed at the start
-      for (int s = 0; s < nseg; ++s) {
-        if (!RESIDENT) load_keys(row, s, key);
-        const uint32_t cand = free_bits(s) & ~marks[s * kST + tid];
-#pragma unroll
-        for (int i = 0; i < kKPT; ++i) {
-          if (((cand >> i) & 1u) && (key[i] >> hs) == (prefix >> hs))
-            atomicAdd(&hist[(key[i] >> shift) & (uint32_t)(nb - 1)], 1);
+      __syncthreads();
+      if (s < P) {
+        const int* reg = ws + kWsReg + (int64_t)s * kRegInts;
+        for (int i = lt; i < sc; i += G) {
+          sh.u.e.kd[so + i] = (uint32_t)reg[i];
+          sh.u.e.kt[so + i] = (uint32_t)reg[kFCap + i];
+          sh.u.e.j[so + i] = reg[2 * kFCap + i];
         }
       }
       __syncthreads();
-      pick_bucket(hist, nb, r, above, sh);
-      prefix |= (uint32_t)sh.pick[0] << shift;
-      above = sh.pick[1];
-    }
-    // every candidate above T, and the first (r - above) equal to T in
-    // index order
-    const uint32_t T = prefix;
-    const int need_eq = r - above;
-    int seen_eq = 0;
-    for (int s = 0; s < nseg; ++s) {
-      if (!RESIDENT) load_keys(row, s, key);
-      const uint32_t cand = free_bits(s) & ~marks[s * kST + tid];
-      uint32_t gt = 0, eq = 0;
+      // this thread's span of the list
+      const int per = (n + kRT - 1) / kRT;
+      const int e0 = tid * per;
+      const int cnt = e0 < n ? (n - e0 < per ? n - e0 : per) : 0;
+      const uint32_t K_d = (uint32_t)ws[kWsKd], K_t = (uint32_t)ws[kWsKt];
+      uint32_t cd = 0;
 #pragma unroll
-      for (int i = 0; i < kKPT; ++i) {
-        const bool c = (cand >> i) & 1u;
-        gt |= (uint32_t)(c && key[i] > T) << i;
-        eq |= (uint32_t)(c && key[i] == T) << i;
-      }
-      int tot;
-      const int before = seen_eq + block_excl_scan(__popc(eq), sh.wsum, &tot);
-      int take = need_eq - before;   // equal keys this thread may still take
-      uint32_t eq_taken = 0;
-      for (uint32_t e = eq; e && take > 0; e &= e - 1, --take) eq_taken |= e & (~e + 1u);
-      marks[s * kST + tid] |= gt | eq_taken;
-      seen_eq += tot;
-    }
-  };
-
-  if (r1 > 0) tier(ds, r1, sh.hist_d, sh.hist_p[0], kd);
-  if (r2 > 0) {
-    if (r1 > 0) {
-      // take the draft tier's picks out of the target histogram
-      for (int s = 0; s < nseg; ++s) {
-        if (!RESIDENT) load_keys(ts, s, kt);
-        const uint32_t m = marks[s * kST + tid];
+      for (int k = 0; k < kEPT; ++k) cd |= (uint32_t)(k < cnt && sh.u.e.kd[e0 + k] >= K_d) << k;
+      int nd;
+      block_excl_scan<true, kRW>(__popc(cd), sh.wsum, &nd);
+      ok = nd >= r1;
+      if (ok && r1 > 0) pd = list_select(sh.u.e.kd, sh.u.e.j, e0, cnt, cd, r1, sh);
+      uint32_t ct = 0;
+      if (ok) {
 #pragma unroll
-        for (int i = 0; i < kKPT; ++i)
-          if ((m >> i) & 1u) atomicSub(&sh.hist_t[kt[i] >> kDigitShift[0]], 1);
+        for (int k = 0; k < kEPT; ++k)
+          ct |= (uint32_t)(k < cnt && rank_of(sh.u.e.kd[e0 + k], sh.u.e.j[e0 + k]) < pd && sh.u.e.kt[e0 + k] >= K_t)
+                << k;
+        int nt;
+        block_excl_scan<true, kRW>(__popc(ct), sh.wsum, &nt);
+        ok = nt >= r2;
+        if (ok && r2 > 0) pt = list_select(sh.u.e.kt, sh.u.e.j, e0, cnt, ct, r2, sh);
       }
-      __syncthreads();
-    }
-    tier(ts, r2, sh.hist_t, sh.hist_p[1], kt);
-  }
-
-  // ascending output: sink, both tiers and window
-  int written = 0;
-  for (int s = 0; s < nseg; ++s) {
-    const int j0 = s * kSeg + tid * kKPT;
-    const uint32_t valid = range_bits(j0, 0, L);
-    const uint32_t sel = (marks[s * kST + tid] | (valid & ~range_bits(j0, lo, hi))) & valid;
-    int tot;
-    const int before = written + block_excl_scan(__popc(sel), sh.wsum, &tot);
-    int pos = before;
-    for (uint32_t e = sel; e; e &= e - 1) {
-      const int i = __ffs(e) - 1;
-      if (pos < p.k_out) out[pos] = j0 + i;
-      ++pos;
-    }
-    written += tot;
-  }
-}
-
-// ---------------------------------------------------------------------------
-// Multi-workgroup selection.  A row of P >= 2 segments of kCSeg tokens is
-// split over P workgroups of kCT threads, one per segment; each holds its
-// segment's keys in registers (thread t: tokens 32t .. 32t+31 of the
-// segment, as above) and runs the same steps as select_kernel.  The
-// workgroups of a row meet at row barriers, where
-//   * the histograms of each radix pass are summed in the row's workspace
-//     (integer atomics of each workgroup's nonzero LDS bins), and every
-//     workgroup reads the sums back and takes the same bucket;
-//   * the counts of equal keys and of output tokens are published per
-//     segment, so each workgroup knows how many precede it in index order.
-// A row barrier is an arrival counter in the workspace: each workgroup adds
-// one and waits until all P have arrived for this phase.  The waits rely on
-// every workgroup of the launch being resident at once: the host takes this
-// kernel only when the occupancy API says the device holds B * P of its
-// workgroups at once (else one workgroup per row).  Work on other streams
-// can still hold CUs, so each wait is bounded: a timeout sets the row's
-// error flag and the wave moves on, so every wave exits; the last workgroup
-// of the row to finish (a counter bumped once its output stores are
-// performed) then overwrites the whole row with -1, which the caller sees in
-// place of a verify set.
-
-#ifndef VA_SEL_CT
-#define VA_SEL_CT 512   // 128: 83 us, 256: 64 us, 512: 58 us, 1024: 69 us on 4 rows of 131072
-#endif
-constexpr int kCT = VA_SEL_CT;             // threads per workgroup
-constexpr int kCWaves = kCT / 64;
-constexpr int kCSeg = kCT * kKPT;          // 16384 tokens per workgroup
-constexpr int kCMaxGroups = 256;           // B * P limit: every workgroup resident (one per CU; two fit)
-constexpr int kSpinLimit = 1 << 18;        // polls per wait (each a device-coherent load: < 1 s)
-
-// Workspace of one row, in ints, zeroed before the launch.
-constexpr int kWsHd = 0;                   // first digit, draft tier [kBins0]
-constexpr int kWsHt = kBins0;              // first digit, target tier [kBins0]
-constexpr int kWsHp = 2 * kBins0;          // later digits [tier][pass - 1][1024]
-constexpr int kWsBar = kWsHp + 4 * 1024;   // arrival counter
-constexpr int kWsErr = kWsBar + 1;         // set when a wait timed out
-constexpr int kWsDone = kWsBar + 2;        // workgroups whose output stores are performed
-constexpr int kWsCnt = kWsBar + 64;        // per segment: equal keys [2][P], output tokens [P]
-
-__host__ __device__ inline int64_t cluster_row_ints(int P) { return ((int64_t)kWsCnt + 3 * P + 63) / 64 * 64; }
-
-struct CShared {
-  int ha[kBins0];     // a workgroup histogram, then the row's sums for a pick
-  int hb[kBins0];
-  int wsum[kCWaves];
-  int pick[2];
-};
-
-__device__ inline int ld_dev(const int* p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
-
-// Returns once every workgroup of the row has reached its `phase`-th
-// barrier (or the wait timed out).  Everything the workgroups exchange is
-// written with agent-scope atomics (performed where every XCD sees them) and
-// read with agent-scope loads, so no cache write-back or invalidation is
-// needed: each wavefront only waits until its own atomics are performed
-// before the workgroup arrives.
-__device__ inline void row_barrier(int* ws, int P, int phase, int spin_limit) {
-  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    __hip_atomic_fetch_add(ws + kWsBar, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const int target = phase * P;
-    for (int spin = 0; ld_dev(ws + kWsBar) < target; ++spin) {
-      if (spin >= spin_limit) {
-        __hip_atomic_store(ws + kWsErr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        break;
-      }
-      __builtin_amdgcn_s_sleep(1);
-    }
-  }
-  __syncthreads();
-}
-
-// pick_bucket for a workgroup of kCT threads: nbins / kCT buckets per
-// thread, highest at the lowest threads.  Two barriers.
-__device__ inline void cpick(const int* hist, int nbins, int r, int above, CShared& sh) {
-  const int tid = threadIdx.x;
-  const int per = nbins / kCT;   // 16 or 4
-  const int top = nbins - per * tid;
-  int csum = 0;
-  for (int k = 0; k < per; ++k) csum += hist[top - 1 - k];
-  int tot;
-  const int cum0 = above + block_excl_scan<false, kCWaves>(csum, sh.wsum, &tot);
-  if (cum0 < r && cum0 + csum >= r) {
-    int cum = cum0, bucket = top - 1;
-    for (int k = 0; k < per; ++k) {
-      const int ck = hist[top - 1 - k];
-      if (cum + ck >= r) {
-        bucket = top - 1 - k;
-        break;
-      }
-      cum += ck;
-    }
-    sh.pick[0] = bucket;
-    sh.pick[1] = cum;
-  }
-  __syncthreads();
-}
-
-__global__ __launch_bounds__(kCT) void select_cluster_kernel(SelParams p, int* ws_all, int P, int spin_limit) {
-  __shared__ CShared sh;
-  const int tid = threadIdx.x;
-  const int b = blockIdx.x / P, seg = blockIdx.x % P;
-  int* ws = ws_all + (int64_t)b * cluster_row_ints(P);
-  const float* ds = p.ds + (int64_t)b * p.ld;
-  const float* ts = p.ts + (int64_t)b * p.ld;
-  int32_t* out = p.out + (int64_t)b * p.k_out;
-  const int L = p.L;
-  const int lo = p.sink < L ? p.sink : L;
-  const int w = p.window < L ? p.window : L;
-  const int hi = L - w > lo ? L - w : lo;
-  const int n_prot = lo + (L - hi);
-  const int rest = p.budget - n_prot;
-  const int n_free = hi - lo;
-  int r1 = p.top_m < rest ? p.top_m : rest;
-  r1 = r1 < n_free ? r1 : n_free;
-  const int r2 = rest - r1;
-  const int j0 = seg * kCSeg + tid * kKPT;
-
-  uint32_t kd[kKPT], kt[kKPT];
-  auto load_keys = [&](const float* row, uint32_t (&key)[kKPT]) __attribute__((always_inline)) {
-    const bool vec = j0 + kKPT <= L && ((reinterpret_cast<uintptr_t>(row + j0) & 15u) == 0);
-    if (vec) {
+      if (ok) {
+        // sink, the listed picks in index order, window
+        uint32_t win = 0;
 #pragma unroll
-      for (int q = 0; q < kKPT / 4; ++q) {
-        const float4 v = *reinterpret_cast<const float4*>(row + j0 + 4 * q);
-        key[4 * q + 0] = order_key(v.x);
-        key[4 * q + 1] = order_key(v.y);
-        key[4 * q + 2] = order_key(v.z);
-        key[4 * q + 3] = order_key(v.w);
+        for (int k = 0; k < kEPT; ++k) {
+          if (k < cnt) {
+            const bool d = rank_of(sh.u.e.kd[e0 + k], sh.u.e.j[e0 + k]) >= pd;
+            const bool t = ((ct >> k) & 1u) && rank_of(sh.u.e.kt[e0 + k], sh.u.e.j[e0 + k]) >= pt;
+            win |= (uint32_t)(d || t) << k;
+          }
+        }
+        int tw;
+        int pos = lo + block_excl_scan<true, kRW>(__popc(win), sh.wsum, &tw);
+#pragma unroll
+        for (int k = 0; k < kEPT; ++k)
+          if (((win >> k) & 1u) && pos < p.k_out) out[pos++] = sh.u.e.j[e0 + k];
+        for (int j = tid; j < lo; j += kRT) out[j] = j;
+        for (int j = tid; j < L - hi; j += kRT) out[lo + r1 + r2 + j] = hi + j;
+        return;
       }
-    } else {
-#pragma unroll
-      for (int i = 0; i < kKPT; ++i) key[i] = j0 + i < L ? order_key(row[j0 + i]) : 0u;
     }
-  };
-  load_keys(ds, kd);
-  load_keys(ts, kt);
-  const uint32_t free = range_bits(j0, lo, hi);
-  uint32_t mark = 0;
-  int phase = 0;
-
-  // first digit of both tiers; the target histogram counts every free token
-  // and is corrected for the draft tier's picks later
-  for (int i = tid; i < kBins0; i += kCT) {
-    sh.ha[i] = 0;
-    sh.hb[i] = 0;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int i = 0; i < kKPT; ++i) {
-    if ((free >> i) & 1u) {
-      if (r1 > 0) atomicAdd(&sh.ha[kd[i] >> kDigitShift[0]], 1);
-      if (r2 > 0) atomicAdd(&sh.hb[kt[i] >> kDigitShift[0]], 1);
-    }
-  }
-  __syncthreads();
-  for (int i = tid; i < kBins0; i += kCT) {
-    if (sh.ha[i]) atomicAdd(ws + kWsHd + i, sh.ha[i]);
-    if (sh.hb[i]) atomicAdd(ws + kWsHt + i, sh.hb[i]);
-  }
-  row_barrier(ws, P, ++phase, spin_limit);
-
-  // Marks the top r candidates (free, not yet marked) of tier ti, whose
-  // row-wide first-digit histogram is g0.
-  auto tier = [&](int ti, int r, const int* g0, uint32_t (&key)[kKPT]) __attribute__((always_inline)) {
-    for (int i = tid; i < kBins0; i += kCT) sh.ha[i] = ld_dev(g0 + i);
     __syncthreads();
-    cpick(sh.ha, kBins0, r, 0, sh);
-    uint32_t prefix = (uint32_t)sh.pick[0] << kDigitShift[0];
-    int above = sh.pick[1];
-    for (int pass = 1; pass < 3; ++pass) {
-      const int shift = kDigitShift[pass];
-      const int nb = 1 << kDigitBits[pass];
-      const int hs = shift + kDigitBits[pass];   // bits above this digit are fixed
-      int* gp = ws + kWsHp + (2 * ti + pass - 1) * 1024;
-      for (int i = tid; i < nb; i += kCT) sh.hb[i] = 0;
-      __syncthreads();
-      const uint32_t cand = free & ~mark;
-#pragma unroll
-      for (int i = 0; i < kKPT; ++i) {
-        if (((cand >> i) & 1u) && (key[i] >> hs) == (prefix >> hs))
-          atomicAdd(&sh.hb[(key[i] >> shift) & (uint32_t)(nb - 1)], 1);
-      }
-      __syncthreads();
-      for (int i = tid; i < nb; i += kCT)
-        if (sh.hb[i]) atomicAdd(gp + i, sh.hb[i]);
-      row_barrier(ws, P, ++phase, spin_limit);
-      for (int i = tid; i < nb; i += kCT) sh.ha[i] = ld_dev(gp + i);
-      __syncthreads();
-      cpick(sh.ha, nb, r, above, sh);
-      prefix |= (uint32_t)sh.pick[0] << shift;
-      above = sh.pick[1];
-    }
-    // every candidate above T, and the first (r - above) equal to T in
-    // index order over the whole row
-    const uint32_t T = prefix;
-    const int need_eq = r - above;
-    const uint32_t cand = free & ~mark;
-    uint32_t gt = 0, eq = 0;
-#pragma unroll
-    for (int i = 0; i < kKPT; ++i) {
-      const bool c = (cand >> i) & 1u;
-      gt |= (uint32_t)(c && key[i] > T) << i;
-      eq |= (uint32_t)(c && key[i] == T) << i;
-    }
-    int tot;
-    const int before = block_excl_scan<true, kCWaves>(__popc(eq), sh.wsum, &tot);
-    if (tid == 0) __hip_atomic_store(ws + kWsCnt + ti * P + seg, tot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    row_barrier(ws, P, ++phase, spin_limit);
-    int prev = 0;   // equal keys in earlier segments
-    for (int q = tid; q < seg; q += kCT) prev += ld_dev(ws + kWsCnt + ti * P + q);
-    int earlier;
-    block_excl_scan<true, kCWaves>(prev, sh.wsum, &earlier);
-    int take = need_eq - earlier - before;
-    uint32_t eq_taken = 0;
-    for (uint32_t e = eq; e && take > 0; e &= e - 1, --take) eq_taken |= e & (~e + 1u);
-    mark |= gt | eq_taken;
-  };
-
-  if (r1 > 0) tier(0, r1, ws + kWsHd, kd);
-  if (r2 > 0) {
-    if (r1 > 0) {
-      // take the draft tier's picks out of the target histogram
-#pragma unroll
-      for (int i = 0; i < kKPT; ++i)
-        if ((mark >> i) & 1u) atomicSub(ws + kWsHt + (kt[i] >> kDigitShift[0]), 1);
-      row_barrier(ws, P, ++phase, spin_limit);
-    }
-    tier(1, r2, ws + kWsHt, kt);
+    pd = kNone;
+    pt = kNone;
   }
-
-  // ascending output: sink, both tiers and window
-  const uint32_t valid = range_bits(j0, 0, L);
-  const uint32_t sel = (mark | (valid & ~free)) & valid;
-  int tot;
-  const int before = block_excl_scan<true, kCWaves>(__popc(sel), sh.wsum, &tot);
-  if (tid == 0) __hip_atomic_store(ws + kWsCnt + 2 * P + seg, tot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  row_barrier(ws, P, ++phase, spin_limit);
-  int prev = 0;
-  for (int q = tid; q < seg; q += kCT) prev += ld_dev(ws + kWsCnt + 2 * P + q);
-  int earlier;
-  block_excl_scan<true, kCWaves>(prev, sh.wsum, &earlier);
-  int pos = earlier + before;
-  for (uint32_t e = sel; e; e &= e - 1) {
-    const int i = __ffs(e) - 1;
-    if (pos < p.k_out) __hip_atomic_store(out + pos, j0 + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    ++pos;
-  }
-  // The last workgroup of the row to get here sees every other workgroup's
-  // output stores performed (agent-scope stores, performed before each
-  // workgroup's count): if any wait of the row timed out, the row is
-  // replaced by -1.
-  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
-  __syncthreads();
-  if (tid == 0) sh.pick[0] = __hip_atomic_fetch_add(ws + kWsDone, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  __syncthreads();
-  if (sh.pick[0] == P - 1 && ld_dev(ws + kWsErr) != 0) {
-    for (int j = tid; j < p.k_out; j += kCT) __hip_atomic_store(out + j, -1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
+  // the exact way over the whole row
+  if (r1 > 0) pd = exact_tier(p, ds, ds, kNone, false, r1, sh);
+  if (r2 > 0) pt = exact_tier(p, ts, ds, pd, true, r2, sh);
+  exact_output(p, ds, ts, out, pd, pt, sh);
 }
 
-__global__ __launch_bounds__(256) void zero_ints_kernel(int* p, int64_t n) {
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = 0;
-}
-
-// Rows that the multi-workgroup kernel takes: budget < L (checked by the
-// caller), longer than one segment of select_kernel (which keeps a
-// one-segment row in registers, while longer rows are re-read on every pass;
-// a row barrier costs a few microseconds), and every workgroup resident at
-// once.  Measured: 16 rows of 32768 tokens 36 us in select_kernel, 53 us
-// here (256-thread workgroups); 4 rows of 131072 tokens 178 us there, 58 us
-// here (64 us with 256-thread workgroups).
-inline int cluster_parts(int32_t B, int32_t L) {
-  const int P = (int)(((int64_t)L + kCSeg - 1) / kCSeg);
-  return L > kSeg && (int64_t)B * P <= kCMaxGroups ? P : 0;
-}
-
-// Workgroups of select_cluster_kernel that the current device holds at once
-// (occupancy per CU times CUs; 0 if it cannot be queried), looked up once
-// per device.
-int cluster_capacity() {
-  constexpr int kDevs = 64;
-  static std::atomic<int> cache[kDevs];   // 0: not looked up yet; else capacity + 1
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return 0;
-  if (dev >= 0 && dev < kDevs) {
-    const int c = cache[dev].load(std::memory_order_relaxed);
-    if (c > 0) return c - 1;
-  }
-  int cus = 0, per_cu = 0;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)select_cluster_kernel, kCT, 0) !=
-          hipSuccess) {
-    (void)hipGetLastError();
-    return 0;
-  }
-  const int cap = cus * per_cu;
-  if (dev >= 0 && dev < kDevs) cache[dev].store(cap + 1, std::memory_order_relaxed);
-  return cap;
-}
-
-// Polls per row-barrier wait: kSpinLimit, or VA_SELECT_SPIN_LIMIT from the
-// environment (a test hook: a limit of 0 makes every early arrival give up
-// at once, which exercises the timeout path).
-int spin_limit() {
-  const char* e = getenv("VA_SELECT_SPIN_LIMIT");
-  if (e == nullptr || *e == '\0') return kSpinLimit;
-  const long v = strtol(e, nullptr, 10);
-  return v < 0 ? 0 : (v > kSpinLimit ? kSpinLimit : (int)v);
+// VA_SELECT_EXACT=1 in the environment makes every call take the exact way
+// (a test hook: both ways must give the same verify set).
+int exact_only() {
+  const char* e = getenv("VA_SELECT_EXACT");
+  return e != nullptr && e[0] == '1';
 }
 
 }  // namespace
 
-size_t select_ws_bytes(int32_t B, int32_t L) {
-  const int P = cluster_parts(B, L);
-  return P ? (size_t)B * cluster_row_ints(P) * sizeof(int) : 0;
-}
+size_t select_ws_bytes(int32_t B, int32_t L) { return (size_t)B * (size_t)row_ints(L) * sizeof(int); }
 
 hipError_t launch_select(const float* draft_score, const float* target_score, int32_t B, int32_t L, int64_t ld,
                          int32_t sink, int32_t window, int32_t top_m, int32_t budget, int32_t* verify_idx,
@@ -643,38 +709,24 @@ hipError_t launch_select(const float* draft_score, const float* target_score, in
   p.out = verify_idx;
   p.ld = ld;
   p.L = L;
-  p.sink = sink;
-  p.window = window;
-  p.top_m = top_m;
   p.budget = budget;
   p.k_out = budget < L ? budget : L;
-  int P = budget < L ? cluster_parts(B, L) : 0;
-  if (P && cluster_capacity() < B * P) P = 0;   // not every workgroup would be resident
-  if (P) {
-    const int64_t n = (int64_t)B * cluster_row_ints(P);
-    const int grid = (int)((n + 255) / 256 < 1024 ? (n + 255) / 256 : 1024);
-    hipLaunchKernelGGL(zero_ints_kernel, dim3(grid), dim3(256), 0, stream, (int*)ws, n);
+  p.lo = sink < L ? sink : L;
+  const int w = window < L ? window : L;
+  p.hi = L - w > p.lo ? L - w : p.lo;
+  p.n_free = p.hi - p.lo;
+  const int rest = budget - (p.lo + (L - p.hi));
+  const int r1 = top_m < rest ? top_m : rest;
+  p.r1 = r1 < p.n_free ? r1 : p.n_free;
+  p.r2 = rest - p.r1;
+  p.exact = exact_only();
+  const int P = filter_parts(L);
+  if (budget < L && !p.exact) {
+    hipLaunchKernelGGL(select_filter_kernel, dim3(B * P), dim3(kFT), 0, stream, p, (int*)ws, P);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    int* ws_i = (int*)ws;
-    int lim = spin_limit();
-    // (a cooperative launch, which would have the runtime guarantee
-    // co-residency, cost ~20 us per call: 56 -> 76 us on 4 rows of 131072)
-    hipLaunchKernelGGL(select_cluster_kernel, dim3(B * P), dim3(kCT), 0, stream, p, ws_i, P, lim);
-    return hipGetLastError();
   }
-  const int nseg = (L + kSeg - 1) / kSeg;
-  const size_t lds = (size_t)(nseg > 0 ? nseg : 1) * kST * sizeof(uint32_t);
-  const bool resident = nseg <= 1;
-  const void* fn = resident ? (const void*)select_kernel<true> : (const void*)select_kernel<false>;
-  if (lds > 48 * 1024) {
-    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-  }
-  if (resident)
-    hipLaunchKernelGGL(select_kernel<true>, dim3(B), dim3(kST), lds, stream, p);
-  else
-    hipLaunchKernelGGL(select_kernel<false>, dim3(B), dim3(kST), lds, stream, p);
+  hipLaunchKernelGGL(select_resolve_kernel, dim3(B), dim3(kRT), 0, stream, p, (const int*)ws, P);
   return hipGetLastError();
 }
 

@@ -31,14 +31,11 @@ def test_verify_mode_and_names():
 
 
 def test_selector_kernel_choice():
-    # one 32768-token segment: the single-workgroup kernel
-    assert bench.select_kernel_name(16, 32768, 2048) == "select_kernel"
-    # longer rows whose 16384-token workgroups all fit at once: several workgroups per row
-    assert bench.select_kernel_name(4, 131072, 4096) == "select_cluster_kernel"
-    assert bench.select_kernel_name(32, 131072, 4096) == "select_cluster_kernel"    # 32 * 8 = 256 groups
-    assert bench.select_kernel_name(33, 131072, 4096) == "select_kernel"            # 264 > 256
-    # budget >= L: every index, no selection kernel of the cluster kind
-    assert bench.select_kernel_name(4, 131072, 131072) == "select_kernel"
+    # a selection: the filter over many workgroups per row, then the resolve
+    assert bench.select_kernel_name(16, 32768, 2048) == "select_filter_kernel+select_resolve_kernel"
+    assert bench.select_kernel_name(4, 131072, 4096) == "select_filter_kernel+select_resolve_kernel"
+    # budget >= L: every index, written by the resolve kernel alone
+    assert bench.select_kernel_name(4, 131072, 131072) == "select_resolve_kernel"
 
 
 def test_algorithmic_counts():
