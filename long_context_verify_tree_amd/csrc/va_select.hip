@@ -138,7 +138,7 @@ __device__ inline int bins_scan(const int* hist, int (&c)[NB / NT], int* wsum, i
 // (cum entries in higher ones), returns its bucket and sets *above to the
 // entries in higher buckets; else -1.
 template <int NT, int NB>
-__device__ inline int bins_find(const int (&c)[NB / NT], int cum, int rank, int* above) {
+__device__ inline int bins_find(const int (&c)[NB / NT], int cum, int rank, int* above, int* count = nullptr) {
   constexpr int PER = NB / NT;
   const int top = NB - PER * (int)threadIdx.x;
   if (rank <= cum) return -1;
@@ -146,6 +146,7 @@ __device__ inline int bins_find(const int (&c)[NB / NT], int cum, int rank, int*
   for (int k = 0; k < PER; ++k) {
     if (rank <= cum + c[k]) {
       *above = cum;
+      if (count) *count = c[k];
       return top - 1 - k;
     }
     cum += c[k];
@@ -351,11 +352,12 @@ struct RShared {
     } e;                      // the row's list, in index order
     int off[kMaxFP];          // (segment offsets, before the list is read)
   } u;
-  int h0[kBins];              // top 12 bits
-  int h1[1024];               // a later digit
+  int h0[2][kBins];           // top 12 bits, one histogram per tier
+  int h1[1024];               // next 10 bits
+  int h2[1024];               // last 10 bits
   uint64_t tiny[kTiny];
   int wsum[kRW];
-  int pick[2];
+  int pick[3];
   int ntiny;
   uint64_t pstar;
 };
@@ -366,16 +368,13 @@ struct RShared {
 // entries (then compared pairwise), else an index-order scan of its ties
 // after the last pass.
 __device__ __forceinline__ uint64_t list_select(const uint32_t* key, const int* jj, int e0, int cnt, uint32_t cand, int r,
-                                RShared& sh) {
+                                int* h0, RShared& sh, bool* ok) {
   const int tid = threadIdx.x;
   uint32_t prefix = 0, fixed = 0;   // key bits found so far, and their mask
   int above = 0;
   for (int pass = 0; pass < 3; ++pass) {
     const int shift = digit_shift(pass), nb = digit_bins(pass);
-    int* hist = pass == 0 ? sh.h0 : sh.h1;
-    for (int i = tid; i < nb; i += kRT) hist[i] = 0;
-    if (tid == 0) sh.ntiny = 0;
-    __syncthreads();
+    int* hist = pass == 0 ? h0 : (pass == 1 ? sh.h1 : sh.h2);
 #pragma unroll
     for (int k = 0; k < kEPT; ++k) {
       if (k < cnt && ((cand >> k) & 1u)) {
@@ -383,26 +382,36 @@ __device__ __forceinline__ uint64_t list_select(const uint32_t* key, const int* 
         if ((kv & fixed) == prefix) atomicAdd(&hist[(kv >> shift) & (uint32_t)(nb - 1)], 1);
       }
     }
+    if (pass < 2) {   // the next pass's histogram
+      int* next = pass == 0 ? sh.h1 : sh.h2;
+      for (int i = tid; i < 1024; i += kRT) next[i] = 0;
+    }
+    if (tid == 0) sh.ntiny = 0;
     __syncthreads();
-    int bk = -1, ab = 0;
+    int bk = -1, ab = 0, bc = 0, t0 = 0;
     if (pass == 0) {
-      int c[kBins / kRT], t;
-      const int cum = above + bins_scan<kRT, kBins>(hist, c, sh.wsum, &t);
-      bk = bins_find<kRT, kBins>(c, cum, r, &ab);
+      int c[kBins / kRT];
+      const int cum = above + bins_scan<kRT, kBins>(hist, c, sh.wsum, &t0);
+      bk = bins_find<kRT, kBins>(c, cum, r, &ab, &bc);
     } else {
       int c[1024 / kRT], t;
       const int cum = above + bins_scan<kRT, 1024>(hist, c, sh.wsum, &t);
-      bk = bins_find<kRT, 1024>(c, cum, r, &ab);
+      bk = bins_find<kRT, 1024>(c, cum, r, &ab, &bc);
     }
     if (bk >= 0) {
       sh.pick[0] = bk;
       sh.pick[1] = ab;
+      sh.pick[2] = bc;
     }
     __syncthreads();
+    if (pass == 0 && t0 < r) {   // fewer candidates than picks (t0: every candidate; uniform)
+      *ok = false;
+      return kNone;
+    }
     prefix |= (uint32_t)sh.pick[0] << shift;
     fixed |= (uint32_t)(nb - 1) << shift;
     above = sh.pick[1];
-    const int E = hist[sh.pick[0] & (nb - 1)];
+    const int E = sh.pick[2];
     if (E <= kTiny) {
       // the bin's entries, compared pairwise
 #pragma unroll
@@ -425,7 +434,6 @@ __device__ __forceinline__ uint64_t list_select(const uint32_t* key, const int* 
       __syncthreads();
       return sh.pstar;
     }
-    __syncthreads();   // (every thread has read the bin's count)
   }
   // more than kTiny entries share the key T = prefix: the (r - above)-th of
   // them in list (index) order is the last taken
@@ -506,7 +514,7 @@ __device__ uint64_t exact_tier(const SelParams p, const float* row, const float*
   int above = 0;
   for (int pass = 0; pass < 3; ++pass) {
     const int shift = digit_shift(pass), nb = digit_bins(pass);
-    int* hist = pass == 0 ? sh.h0 : sh.h1;
+    int* hist = pass == 0 ? sh.h0[0] : sh.h1;
     for (int i = tid; i < nb; i += kRT) hist[i] = 0;
     __syncthreads();
     for (int s = 0; s < nseg; ++s) {
@@ -617,6 +625,10 @@ __global__ __launch_bounds__(kRT) void select_resolve_kernel(SelParams p, const 
     if (ok) {
       // gather the regions into LDS in index order, G threads per region
       if (tid < P) sh.u.off[tid] = off;
+      for (int i = tid; i < kBins; i += kRT) {
+        sh.h0[0][i] = 0;
+        sh.h0[1][i] = 0;
+      }
       __syncthreads();
       const int G = kRT / P;
       const int s = tid / G, lt = tid % G;
@@ -628,10 +640,24 @@ __global__ __launch_bounds__(kRT) void select_resolve_kernel(SelParams p, const 
       __syncthreads();
       if (s < P) {
         const int* reg = ws + kWsReg + (int64_t)s * kRegInts;
-        for (int i = lt; i < sc; i += G) {
-          sh.u.e.kd[so + i] = (uint32_t)reg[i];
-          sh.u.e.kt[so + i] = (uint32_t)reg[kFCap + i];
-          sh.u.e.j[so + i] = reg[2 * kFCap + i];
+        for (int i0 = lt; i0 < sc; i0 += 4 * G) {   // four entries in flight
+          uint32_t a[4], t[4];
+          int jj[4];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const int i = i0 + u * G < sc ? i0 + u * G : i0;
+            a[u] = (uint32_t)reg[i];
+            t[u] = (uint32_t)reg[kFCap + i];
+            jj[u] = reg[2 * kFCap + i];
+          }
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            if (i0 + u * G < sc) {
+              sh.u.e.kd[so + i0 + u * G] = a[u];
+              sh.u.e.kt[so + i0 + u * G] = t[u];
+              sh.u.e.j[so + i0 + u * G] = jj[u];
+            }
+          }
         }
       }
       __syncthreads();
@@ -643,20 +669,14 @@ __global__ __launch_bounds__(kRT) void select_resolve_kernel(SelParams p, const 
       uint32_t cd = 0;
 #pragma unroll
       for (int k = 0; k < kEPT; ++k) cd |= (uint32_t)(k < cnt && sh.u.e.kd[e0 + k] >= K_d) << k;
-      int nd;
-      block_excl_scan<true, kRW>(__popc(cd), sh.wsum, &nd);
-      ok = nd >= r1;
-      if (ok && r1 > 0) pd = list_select(sh.u.e.kd, sh.u.e.j, e0, cnt, cd, r1, sh);
+      if (r1 > 0) pd = list_select(sh.u.e.kd, sh.u.e.j, e0, cnt, cd, r1, sh.h0[0], sh, &ok);
       uint32_t ct = 0;
       if (ok) {
 #pragma unroll
         for (int k = 0; k < kEPT; ++k)
           ct |= (uint32_t)(k < cnt && rank_of(sh.u.e.kd[e0 + k], sh.u.e.j[e0 + k]) < pd && sh.u.e.kt[e0 + k] >= K_t)
                 << k;
-        int nt;
-        block_excl_scan<true, kRW>(__popc(ct), sh.wsum, &nt);
-        ok = nt >= r2;
-        if (ok && r2 > 0) pt = list_select(sh.u.e.kt, sh.u.e.j, e0, cnt, ct, r2, sh);
+        if (r2 > 0) pt = list_select(sh.u.e.kt, sh.u.e.j, e0, cnt, ct, r2, sh.h0[1], sh, &ok);
       }
       if (ok) {
         // sink, the listed picks in index order, window
