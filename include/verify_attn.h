@@ -162,7 +162,9 @@ va_status verify_attn_sparse(const va_attn_desc* desc,
 
 /* The two stages that verify_attn_dense / verify_attn_sparse enqueue, for
  * callers that time or schedule them separately.  verify_attn_partials
- * writes the split context partials and the tree partial into ws
+ * writes the split context partials and the tree partial into ws (the
+ * shared-tile kernel, when the context has splits, walks the tree in the
+ * same workgroup as the last split and writes no separate tree partial)
  * (verify_idx == NULL: dense over [0, L) and K is ignored; otherwise sparse
  * over the K indices); verify_attn_merge joins them into out / lse.  The
  * merge must be given the same desc and ws and n_ctx = L (dense) or K
@@ -212,7 +214,8 @@ va_status build_draft_tree(const float* cand_prob, const int32_t* cand_token, in
  * here is the kernels'): with R = (Hq / Hkv) N query rows per KV head cut
  * into row tiles of `rows` rows (256 in the shared-tile kernel: bf16 with
  * R > 64; else 32, or 64 for float32 with R > 32) and the context cut into
- * the call's splits (parts = splits + 1, the tree),
+ * the call's splits (parts = splits + 1 for the tree, or splits when the
+ * shared-tile kernel walks the tree with the last split),
  *     T = max(KV / bandwidth, Q F_pad / compute_k) + W / bandwidth + overhead
  * KV = 2 B Hkv n_ctx D e, F_pad = 4 B Hkv tiles rows n_ctx D (padded rows
  * included), compute_k = compute_shared or compute_tiles by kernel,

@@ -111,7 +111,13 @@ va::Plan make_plan(const va_attn_desc* d, int32_t n_ctx) {
   if (len < VA_MIN_SPLIT) len = VA_MIN_SPLIT;
   pl.split_len = (int)len;
   pl.n_ctx_splits = n_ctx > 0 ? (int)((n_ctx + len - 1) / len) : 0;
-  pl.n_parts = pl.n_ctx_splits + 1;
+  // The shared-tile kernel runs one workgroup per CU: the tree rides on the
+  // last context split's workgroup (after its context keys), so the grid is
+  // the context workgroups alone and each row has one partial row fewer.
+  // The per-wavefront kernels keep the tree as a part of its own (short
+  // workgroups that start first).
+  pl.tree_in_last = pl.rb == va::kRowsKernel && pl.n_ctx_splits > 0;
+  pl.n_parts = pl.n_ctx_splits + (pl.tree_in_last ? 0 : 1);
   pl.rows = (int64_t)d->B * d->Hq * d->N;
   const size_t o_bytes = (size_t)pl.rows * pl.n_parts * d->D * sizeof(float);
   pl.off_lse = align_up(o_bytes);
@@ -173,6 +179,7 @@ va_status run_partials(const va_attn_desc* d, const void* q, const void* kc, con
   p.split_len = pl.split_len;
   p.n_ctx_splits = pl.n_ctx_splits;
   p.n_parts = pl.n_parts;
+  p.tree_in_last = pl.tree_in_last;
   p.total_groups = (int)groups;
   p.c = eff_scale(d) * 1.4426950408889634f;
   hipError_t e = va::launch_partials(p, d->dtype, d->D, pl.rb, gather, stream);

@@ -63,7 +63,7 @@ constexpr int kAncWords = kMaxN / 32;
 __device__ inline void decode_group(const PartialParams& p, int& rt, int& part, int& kvh, int& b) {
   int id;
   if (VA_TREE_FIRST) {
-    const int ntree = p.B * p.Hkv * p.row_tiles;
+    const int ntree = p.tree_in_last ? 0 : p.B * p.Hkv * p.row_tiles;
     if ((int)blockIdx.x < ntree) {
       id = blockIdx.x;
       rt = id % p.row_tiles;
@@ -623,10 +623,16 @@ void rows_kernel(PartialParams p) {
 
   int rt, part, kvh, b;
   decode_group(p, rt, part, kvh, b);
+  // tree: a part of the draft tree alone (no context); tree_after: the last
+  // context split, which walks the draft tree after its context keys
   const bool tree = part == p.n_ctx_splits;
+  const bool tree_after = p.tree_in_last && part == p.n_ctx_splits - 1;
   const int row0 = rt * GROWS;
 
-  if (tree) {
+  // ancestor bitmask of each of the workgroup's rows over the draft nodes
+  // (read only by the tree walk; the last context split builds it once its
+  // context keys are done, so its context walk starts with the others)
+  auto build_anc = [&]() __attribute__((always_inline)) {
     for (int j = tid; j < p.N; j += kRowsThreads) par[j] = p.parent[(int64_t)b * p.N + j];
     for (int j = tid; j < GROWS * kAncWords; j += kRowsThreads) (&anc[0][0])[j] = 0u;
     __syncthreads();
@@ -638,10 +644,9 @@ void rows_kernel(PartialParams p) {
         j = (pj >= -1 && pj < j) ? pj : -1;  // malformed parents end the path
       }
     }
-  } else {
-    for (int j = tid; j < GROWS * kAncWords; j += kRowsThreads) (&anc[0][0])[j] = ~0u;
-  }
-  __syncthreads();
+    __syncthreads();
+  };
+  if (tree) build_anc();
 
   // queries of this wavefront's 32 rows as MFMA B operands (Q^T)
   const int myrow = row0 + 32 * wave + n;
@@ -657,31 +662,45 @@ void rows_kernel(PartialParams p) {
     }
   }
 
-  const T* kbase;
-  const T* vbase;
+  // the region a walk reads: this split's context keys, or the draft tree
   uint32_t kts_b, vts_b;     // bytes between consecutive keys
-  int kb, ke, region;        // key range of the part; keys addressable in the region
-  if (tree) {
-    kbase = (const T*)p.kd + (int64_t)b * p.kds[0] + (int64_t)kvh * p.kds[1];
-    vbase = (const T*)p.vd + (int64_t)b * p.vds[0] + (int64_t)kvh * p.vds[1];
-    kts_b = (uint32_t)(p.kds[2] * 2);
-    vts_b = (uint32_t)(p.vds[2] * 2);
-    kb = 0;
-    ke = region = p.N;
-  } else {
-    kbase = (const T*)p.kc + (int64_t)b * p.kcs[0] + (int64_t)kvh * p.kcs[1];
-    vbase = (const T*)p.vc + (int64_t)b * p.vcs[0] + (int64_t)kvh * p.vcs[1];
-    kts_b = (uint32_t)(p.kcs[2] * 2);
-    vts_b = (uint32_t)(p.vcs[2] * 2);
-    kb = part * p.split_len;
-    ke = min(p.n_ctx, kb + p.split_len);
-    region = p.L;
-  }
-  const rsrc_t krs = make_rsrc(kbase, (uint32_t)region * kts_b);
-  const rsrc_t vrs = make_rsrc(vbase, (uint32_t)region * vts_b);
-  const bool gather = GATHER && !tree;
+  int kb, ke;                // key range of the walk
+  rsrc_t krs, vrs;
+  bool gather;
+  int ntiles, nrot, rot;
   const rsrc_t irs = make_rsrc(GATHER ? p.idx + (int64_t)b * p.idx_stride : p.idx, GATHER ? (uint32_t)p.n_ctx * 4u : 0u);
-  const int ntiles = ke > kb ? (ke - kb + kTileKeys - 1) / kTileKeys : 0;
+  auto set_region = [&](bool tr) __attribute__((always_inline)) {
+    const T* kbase;
+    const T* vbase;
+    int region;              // keys addressable in the region
+    if (tr) {
+      kbase = (const T*)p.kd + (int64_t)b * p.kds[0] + (int64_t)kvh * p.kds[1];
+      vbase = (const T*)p.vd + (int64_t)b * p.vds[0] + (int64_t)kvh * p.vds[1];
+      kts_b = (uint32_t)(p.kds[2] * 2);
+      vts_b = (uint32_t)(p.vds[2] * 2);
+      kb = 0;
+      ke = region = p.N;
+    } else {
+      kbase = (const T*)p.kc + (int64_t)b * p.kcs[0] + (int64_t)kvh * p.kcs[1];
+      vbase = (const T*)p.vc + (int64_t)b * p.vcs[0] + (int64_t)kvh * p.vcs[1];
+      kts_b = (uint32_t)(p.kcs[2] * 2);
+      vts_b = (uint32_t)(p.vcs[2] * 2);
+      kb = part * p.split_len;
+      ke = min(p.n_ctx, kb + p.split_len);
+      region = p.L;
+    }
+    krs = make_rsrc(kbase, (uint32_t)region * kts_b);
+    vrs = make_rsrc(vbase, (uint32_t)region * vts_b);
+    gather = GATHER && !tr;
+    ntiles = ke > kb ? (ke - kb + kTileKeys - 1) / kTileKeys : 0;
+    // Tile t of the walk.  Whole context tiles (all but a partial last one)
+    // start at a per-head offset, so heads do not read the same DRAM
+    // channels in step; the partial tile comes last; past the end a slot
+    // re-fetches the last tile, never staged.
+    nrot = tr ? 0 : (ke - kb) / kTileKeys;
+    rot = VA_ROTATE && nrot > 0 ? (int)((int64_t)(b * p.Hkv + kvh) * nrot / ((int64_t)p.B * p.Hkv)) : 0;
+  };
+  set_region(tree);
 
   // Thread chunk j of a tile: combined index tid + 512 j; the first KCH are
   // K chunks, the rest V chunks.  Every chunk of a thread lies in the same
@@ -693,12 +712,6 @@ void rows_kernel(PartialParams p) {
   u32x4 rg[RING][NCT];
   bool okr[RING];   // the thread's key exists (tile slot)
   int ixr[RING];    // gathered index of the thread's key in the tile the slot loads next
-  // Tile t of the part's walk.  Whole context tiles (all but a partial last
-  // one) start at a per-head offset, so heads do not read the same DRAM
-  // channels in step; the partial tile comes last; past the end a slot
-  // re-fetches the last tile, never staged.
-  const int nrot = tree ? 0 : (ke - kb) / kTileKeys;
-  const int rot = VA_ROTATE && nrot > 0 ? (int)((int64_t)(b * p.Hkv + kvh) * nrot / ((int64_t)p.B * p.Hkv)) : 0;
   auto clamp_tile = [&](int t) __attribute__((always_inline)) -> int {
     if (t < nrot) {
       const int tr = t + rot;
@@ -759,11 +772,15 @@ void rows_kernel(PartialParams p) {
     return s;
   };
   // online softmax of tile t's scores s, then O^T += V^T P^T
-  auto soft_pv = [&](f32x16 s, int t, int buf, auto masked_tag) __attribute__((always_inline)) {
-    constexpr bool MASKED = decltype(masked_tag)::value;
+  // mask_tag: 0 no mask (whole context tiles), 1 the tile's existing keys
+  // (a partial context tile), 2 existing keys that are ancestors (the tree)
+  auto soft_pv = [&](f32x16 s, int t, int buf, auto mask_tag) __attribute__((always_inline)) {
+    constexpr int MK = decltype(mask_tag)::value;
+    constexpr bool MASKED = MK != 0;
     const T* vt = stage + buf * STAGE_ELEMS + TILE_ELEMS;
     uint32_t key_bits = ~0u;
-    if constexpr (MASKED)
+    if constexpr (MK == 1) key_bits = (uint32_t)__ballot(kval[buf][n] != 0 && h == 0);
+    if constexpr (MK == 2)
       key_bits = (uint32_t)__ballot(kval[buf][n] != 0 && h == 0) & anc[32 * wave + n][t & (kAncWords - 1)];
 
     float tmax = -INFINITY;
@@ -826,20 +843,25 @@ void rows_kernel(PartialParams p) {
   // while tile t is processed, so the QK MFMAs of tile t+1 are issued
   // before the softmax of tile t and run under it; then tile t+2 is staged
   // into the buffer tile t-1 used.
-  // prologue: tiles 0..RING-1 in flight, tiles 0 and 1 staged, S of tile 0
+  // prologue of a walk: tiles 0..RING-1 in flight, tiles 0 and 1 staged, S
+  // of tile 0
+  f32x16 s_cur;
+  auto prologue = [&]() __attribute__((always_inline)) {
 #pragma unroll
-  for (int pp = 0; pp < RING; ++pp) {
-    load(pp, load_idx(pp), rg[pp], okr[pp]);
-    ixr[pp] = load_idx(pp + RING);
-  }
+    for (int pp = 0; pp < RING; ++pp) {
+      load(pp, load_idx(pp), rg[pp], okr[pp]);
+      ixr[pp] = load_idx(pp + RING);
+    }
 #pragma unroll
-  for (int pp = 0; pp < 2; ++pp) {
-    stage_write(rg[pp], okr[pp], pp);
-    load(RING + pp, ixr[pp], rg[pp], okr[pp]);
-    ixr[pp] = load_idx(2 * RING + pp);
-  }
-  lds_barrier();
-  f32x16 s_cur = qk(0);
+    for (int pp = 0; pp < 2; ++pp) {
+      stage_write(rg[pp], okr[pp], pp);
+      load(RING + pp, ixr[pp], rg[pp], okr[pp]);
+      ixr[pp] = load_idx(2 * RING + pp);
+    }
+    lds_barrier();
+    s_cur = qk(0);
+  };
+  prologue();
   auto tile_loop = [&](int t_end, auto masked_tag) __attribute__((always_inline)) {
     int t0 = 0;
     for (; t0 + RING <= t_end; t0 += RING) {
@@ -870,16 +892,24 @@ void rows_kernel(PartialParams p) {
     }
   };
   if (tree) {
-    tile_loop(ntiles, std::true_type{});
+    tile_loop(ntiles, std::integral_constant<int, 2>{});
   } else {
     // whole context tiles (dense or gathered) without the mask, then the
     // partial tail tile (staged in buffer nfull % NSTAGE, its S in s_cur)
-    // with it.  A gathered index outside [0, L) in a whole tile reads as a
-    // zero key and value row (a precondition violation: memory-safe, result
-    // unspecified but finite).
+    // with its existing keys.  A gathered index outside [0, L) in a whole
+    // tile reads as a zero key and value row (a precondition violation:
+    // memory-safe, result unspecified but finite).
     const int nfull = (ke - kb) / kTileKeys;
-    tile_loop(nfull, std::false_type{});
-    if (nfull < ntiles) soft_pv(s_cur, nfull, nfull % NSTAGE, std::true_type{});
+    tile_loop(nfull, std::integral_constant<int, 0>{});
+    if (nfull < ntiles) soft_pv(s_cur, nfull, nfull % NSTAGE, std::integral_constant<int, 1>{});
+    if (tree_after) {
+      // the draft tree, continuing this split's running softmax (every
+      // wavefront is done with the stages first)
+      build_anc();
+      set_region(true);
+      prologue();
+      tile_loop(ntiles, std::integral_constant<int, 2>{});
+    }
   }
 
   // this wavefront's rows: normalised partial and log2-sum-exp

@@ -26,7 +26,8 @@ struct Plan {
   int row_tiles;     // ceil(G * N / (32 * rb))
   int split_len;     // context keys per split (multiple of 128)
   int n_ctx_splits;  // ceil(n_ctx / split_len); 0 when n_ctx == 0
-  int n_parts;       // n_ctx_splits + 1 (the tree part is last)
+  int n_parts;       // n_ctx_splits + 1 (the tree part is last), or n_ctx_splits when tree_in_last
+  int tree_in_last;  // the shared-tile kernel's last split also walks the draft tree
   int64_t rows;      // B * Hq * N output rows
   size_t off_lse;    // byte offset of the partial lse array in the workspace
   size_t ws_bytes;   // total workspace bytes
@@ -47,6 +48,7 @@ struct PartialParams {
   int B, Hq, Hkv, G, N, L, n_ctx;
   int R;                // G * N
   int row_tiles, split_len, n_ctx_splits, n_parts;
+  int tree_in_last;     // no tree part: the last context split walks the tree too
   int total_groups;     // grid size
   float c;              // scale * log2(e)
 };

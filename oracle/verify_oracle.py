@@ -462,9 +462,11 @@ def kernel_plan(B: int, Hq: int, Hkv: int, n_ctx: int, N: int, elem_bytes: int):
     of 256 rows (the shared-tile kernel, bf16 with more than 64 rows), else
     32 rows (bf16), else 32 or 64 rows (fp32, 64 when more than 32 rows);
     the context keys go in splits sized for about one context workgroup per
-    CU of a 256-CU device (splits of a multiple of 128 keys, at least 512),
-    and the tree is one more part.  Returns (shared_tile_kernel, rows per
-    tile, row tiles per KV head, context splits, parts)."""
+    CU of a 256-CU device (splits of a multiple of 128 keys, at least 512).
+    The tree is one more part, except in the shared-tile kernel, whose last
+    context split walks the tree after its context keys (one part when there
+    is no context).  Returns (shared_tile_kernel, rows per tile, row tiles
+    per KV head, context splits, parts)."""
     R = (Hq // Hkv) * N
     shared = elem_bytes == 2 and R > 64
     if shared:
@@ -479,7 +481,7 @@ def kernel_plan(B: int, Hq: int, Hkv: int, n_ctx: int, N: int, elem_bytes: int):
     split = -(-n_ctx // want) if n_ctx > 0 else 128
     split = max(512, -(-split // 128) * 128)
     splits = -(-n_ctx // split) if n_ctx > 0 else 0
-    return shared, rows, tiles, splits, splits + 1
+    return shared, rows, tiles, splits, splits if shared and splits > 0 else splits + 1
 
 
 def verify_time_plan(B: int, Hq: int, Hkv: int, D: int, n_ctx: int, N: int, elem_bytes: int,

@@ -848,13 +848,16 @@ def test_kernel_plan_hand_cases():
     # N = 16: 64 rows, still the per-wavefront kernel, two 32-row tiles ->
     # 128 pairs -> 2 splits of 16384
     assert vo.kernel_plan(8, 32, 8, 32768, 16, 2) == (False, 32, 2, 2, 3)
-    # N = 17: 68 rows -> the shared-tile kernel, one 256-row tile
-    assert vo.kernel_plan(8, 32, 8, 32768, 17, 2) == (True, 256, 1, 4, 5)
+    # N = 17: 68 rows -> the shared-tile kernel, one 256-row tile; its last
+    # split walks the tree, so the parts are the splits
+    assert vo.kernel_plan(8, 32, 8, 32768, 17, 2) == (True, 256, 1, 4, 4)
     # N = 65: 260 rows -> two 256-row tiles -> 128 pairs -> 2 splits
-    assert vo.kernel_plan(8, 32, 8, 32768, 65, 2) == (True, 256, 2, 2, 3)
+    assert vo.kernel_plan(8, 32, 8, 32768, 65, 2) == (True, 256, 2, 2, 2)
     # 70B shape (G = 8), batch 4, 131072 keys, N = 128: 1024 rows, 4 tiles,
     # 128 pairs -> 2 splits of 65536
-    assert vo.kernel_plan(4, 64, 8, 131072, 128, 2) == (True, 256, 4, 2, 3)
+    assert vo.kernel_plan(4, 64, 8, 131072, 128, 2) == (True, 256, 4, 2, 2)
+    # the shared-tile kernel with no context: the tree alone
+    assert vo.kernel_plan(4, 64, 8, 0, 128, 2) == (True, 256, 4, 0, 1)
     # short context: splits never below 512 keys; no context: only the tree part
     assert vo.kernel_plan(1, 4, 1, 700, 8, 2) == (False, 32, 1, 2, 3)
     assert vo.kernel_plan(1, 4, 1, 0, 8, 2) == (False, 32, 1, 0, 1)
@@ -873,20 +876,21 @@ def test_plan_time_model_closed_forms():
     assert vo.verify_time_plan(N=8, bandwidth=bw, compute_shared=cs, compute_tiles=ct, overhead=c0, **args) == \
         pytest.approx(kv / bw + w8 / bw + c0, rel=1e-12)
     # N = 64: one 256-row tile of the shared-tile kernel (256 rows, no
-    # padding): compute 4 * 8 * 8 * 256 * 32768 * 128 flops at cs
+    # padding): compute 4 * 8 * 8 * 256 * 32768 * 128 flops at cs; 4 parts
+    # (the tree rides on the last split)
     f = 4 * 8 * 8 * 256 * 32768 * 128
-    w64 = 2 * 8 * 32 * 64 * 5 * 129 * 4
+    w64 = 2 * 8 * 32 * 64 * 4 * 129 * 4
     assert vo.verify_time_plan(N=64, bandwidth=bw, compute_shared=cs, compute_tiles=ct, overhead=c0, **args) == \
         pytest.approx(max(kv / bw, f / cs) + w64 / bw + c0, rel=1e-12)
     # N = 33 and N = 64 run the same padded work (one 256-row tile): they
     # differ only in the partial rows
     t33 = vo.verify_time_plan(N=33, bandwidth=bw, compute_shared=cs, compute_tiles=ct, overhead=0.0, **args)
     t64 = vo.verify_time_plan(N=64, bandwidth=bw, compute_shared=cs, compute_tiles=ct, overhead=0.0, **args)
-    assert t64 - t33 == pytest.approx(2 * 8 * 32 * (64 - 33) * 5 * 129 * 4 / bw, rel=1e-9)
+    assert t64 - t33 == pytest.approx(2 * 8 * 32 * (64 - 33) * 4 * 129 * 4 / bw, rel=1e-9)
     # one more node past a tile boundary adds a whole tile of padded work
     t65 = vo.verify_time_plan(N=65, bandwidth=bw, compute_shared=cs, compute_tiles=ct, overhead=0.0, **args)
-    assert t65 - t64 == pytest.approx((f / cs) * (2 - 1) - 2 * 8 * 32 * 64 * 5 * 129 * 4 / bw
-                                      + 2 * 8 * 32 * 65 * 3 * 129 * 4 / bw, rel=1e-9)
+    assert t65 - t64 == pytest.approx((f / cs) * (2 - 1) - 2 * 8 * 32 * 64 * 4 * 129 * 4 / bw
+                                      + 2 * 8 * 32 * 65 * 2 * 129 * 4 / bw, rel=1e-9)
     # grid rounds: 70B shape, 4 sequences.  N = 96: 768 rows -> 3 tiles, 96
     # (b, kvh, tile) pairs -> 3 splits -> 288 context workgroups, 2 rounds of
     # 256 where 1.125 would do: the compute term is 512 / 288 of the padded
@@ -894,7 +898,7 @@ def test_plan_time_model_closed_forms():
     a70 = dict(B=4, Hq=64, Hkv=8, D=128, n_ctx=131072, elem_bytes=2)
     big_c = dict(bandwidth=1e30, compute_shared=1e15, compute_tiles=1e15, overhead=0.0)
     f96 = 4 * 4 * 8 * 3 * 256 * 131072 * 128
-    w96 = 2 * 4 * 64 * 96 * 4 * 129 * 4
+    w96 = 2 * 4 * 64 * 96 * 3 * 129 * 4
     assert vo.verify_time_plan(N=96, **a70, **big_c) == pytest.approx(512 / 288 * f96 / 1e15 + w96 / 1e30, rel=1e-12)
     f128 = 4 * 4 * 8 * 4 * 256 * 131072 * 128
     assert vo.verify_time_plan(N=128, **a70, **big_c) == pytest.approx(f128 / 1e15, rel=1e-12)
