@@ -93,24 +93,39 @@ va::Plan make_plan(const va_attn_desc* d, int32_t n_ctx) {
   const int rows_per_tile = pl.rb == va::kRowsKernel ? 256 : 32 * pl.rb;
   pl.row_tiles = (R + rows_per_tile - 1) / rows_per_tile;
   const int64_t pairs = (int64_t)d->B * d->Hkv * pl.row_tiles;
-  // About one context workgroup per CU (the partial kernels run one
-  // workgroup per CU), i.e. a single round with no second wave of
-  // workgroups starting late, but no split shorter than 512 keys: every
-  // split costs one partial row per query row in the workspace.
+  // Context splits.  The partial kernels run about one workgroup per CU,
+  // so the context workgroups run in rounds of 256, each round as long as
+  // its splits.  Of the split counts up to twice the one that first reaches
+  // 256 workgroups, take the one whose rounds finish first (rounds x keys
+  // per split, after rounding a split to a multiple of 128 keys and at least
+  // 512), the fewest splits on a tie: every split costs one partial row per
+  // query row in the workspace.  (Reaching 256 workgroups alone can leave a
+  // few in a second round on an idle chip: 96 pairs in 3 splits are 288
+  // workgroups, two rounds of a third of the context; 5 splits take two
+  // rounds of a fifth.)
 #ifndef VA_TARGET_GROUPS
 #define VA_TARGET_GROUPS 256
 #endif
-  const int64_t target_groups = VA_TARGET_GROUPS;
-  int64_t want_splits = (target_groups + pairs - 1) / pairs;
-  if (want_splits < 1) want_splits = 1;
-  int64_t len = n_ctx > 0 ? (n_ctx + want_splits - 1) / want_splits : 128;
-  len = (len + 127) / 128 * 128;
 #ifndef VA_MIN_SPLIT
 #define VA_MIN_SPLIT 512
 #endif
-  if (len < VA_MIN_SPLIT) len = VA_MIN_SPLIT;
-  pl.split_len = (int)len;
-  pl.n_ctx_splits = n_ctx > 0 ? (int)((n_ctx + len - 1) / len) : 0;
+  const int64_t target_groups = VA_TARGET_GROUPS;
+  const int64_t s0 = pairs < target_groups ? (target_groups + pairs - 1) / pairs : 1;
+  int64_t best_len = VA_MIN_SPLIT, best_splits = 0, best_cost = -1;
+  for (int64_t s = 1; s <= 2 * s0 && n_ctx > 0; ++s) {
+    int64_t len = (n_ctx + s - 1) / s;
+    len = (len + 127) / 128 * 128;
+    if (len < VA_MIN_SPLIT) len = VA_MIN_SPLIT;
+    const int64_t splits = (n_ctx + len - 1) / len;
+    const int64_t cost = (pairs * splits + target_groups - 1) / target_groups * len;
+    if (best_cost < 0 || cost < best_cost) {
+      best_cost = cost;
+      best_len = len;
+      best_splits = splits;
+    }
+  }
+  pl.split_len = (int)best_len;
+  pl.n_ctx_splits = (int)best_splits;
   // The shared-tile kernel runs one workgroup per CU: the tree rides on the
   // last context split's workgroup (after its context keys), so the grid is
   // the context workgroups alone and each row has one partial row fewer.

@@ -461,8 +461,9 @@ def kernel_plan(B: int, Hq: int, Hkv: int, n_ctx: int, N: int, elem_bytes: int):
     plan, restated here): the G * N query rows of a KV head go in row tiles
     of 256 rows (the shared-tile kernel, bf16 with more than 64 rows), else
     32 rows (bf16), else 32 or 64 rows (fp32, 64 when more than 32 rows);
-    the context keys go in splits sized for about one context workgroup per
-    CU of a 256-CU device (splits of a multiple of 128 keys, at least 512).
+    the context keys go in splits of a multiple of 128 keys (at least 512),
+    their count chosen for the soonest end of the context workgroups' rounds
+    on a 256-CU device running one workgroup per CU.
     The tree is one more part, except in the shared-tile kernel, whose last
     context split walks the tree after its context keys (one part when there
     is no context).  Returns (shared_tile_kernel, rows per tile, row tiles
@@ -477,10 +478,18 @@ def kernel_plan(B: int, Hq: int, Hkv: int, n_ctx: int, N: int, elem_bytes: int):
         rows = 64
     tiles = -(-R // rows)
     pairs = B * Hkv * tiles
-    want = max(1, -(-256 // pairs))
-    split = -(-n_ctx // want) if n_ctx > 0 else 128
-    split = max(512, -(-split // 128) * 128)
-    splits = -(-n_ctx // split) if n_ctx > 0 else 0
+    # context splits: of 1 .. 2 s0 splits (s0 the fewest that make 256
+    # workgroups), the count whose rounds of 256 workgroups end first
+    # (rounds times keys per split), the fewest on a tie
+    s0 = -(-256 // pairs) if pairs < 256 else 1
+    splits, best = 0, None
+    for s in range(1, 2 * s0 + 1) if n_ctx > 0 else ():
+        per = -(-n_ctx // s)                        # ceil(n_ctx / s)
+        split = max(512, -(-per // 128) * 128)      # a multiple of 128, >= 512
+        cnt = -(-n_ctx // split)
+        cost = -(-(pairs * cnt) // 256) * split
+        if best is None or cost < best:
+            best, splits = cost, cnt
     return shared, rows, tiles, splits, splits if shared and splits > 0 else splits + 1
 
 

@@ -858,6 +858,13 @@ def test_kernel_plan_hand_cases():
     assert vo.kernel_plan(4, 64, 8, 131072, 128, 2) == (True, 256, 4, 2, 2)
     # the shared-tile kernel with no context: the tree alone
     assert vo.kernel_plan(4, 64, 8, 0, 128, 2) == (True, 256, 4, 0, 1)
+    # N = 96: 768 rows, 3 tiles, 96 pairs.  Rounds of 256 workgroups times
+    # keys per split, for 1..6 splits: 1 round x 131072, 1 x 65536, 2 x 43776
+    # (288 workgroups), 2 x 32768, 2 x 26240 (480), 3 x 21888 -> 5 splits
+    assert vo.kernel_plan(4, 64, 8, 131072, 96, 2) == (True, 256, 3, 5, 5)
+    # 200 pairs (25 sequences, one tile each): 1 to 4 splits all take one
+    # context length in all (1 x L, 2 x L/2, ...) -> the fewest, 1
+    assert vo.kernel_plan(25, 32, 8, 32768, 8, 2) == (False, 32, 1, 1, 2)
     # short context: splits never below 512 keys; no context: only the tree part
     assert vo.kernel_plan(1, 4, 1, 700, 8, 2) == (False, 32, 1, 2, 3)
     assert vo.kernel_plan(1, 4, 1, 0, 8, 2) == (False, 32, 1, 0, 1)
@@ -892,17 +899,18 @@ def test_plan_time_model_closed_forms():
     assert t65 - t64 == pytest.approx((f / cs) * (2 - 1) - 2 * 8 * 32 * 64 * 4 * 129 * 4 / bw
                                       + 2 * 8 * 32 * 65 * 2 * 129 * 4 / bw, rel=1e-9)
     # grid rounds: 70B shape, 4 sequences.  N = 96: 768 rows -> 3 tiles, 96
-    # (b, kvh, tile) pairs -> 3 splits -> 288 context workgroups, 2 rounds of
-    # 256 where 1.125 would do: the compute term is 512 / 288 of the padded
-    # work's; N = 128: 4 tiles, 2 splits, 256 workgroups, one round.
+    # (b, kvh, tile) pairs -> 5 splits -> 480 context workgroups in 2 rounds
+    # of 256 where 1.875 would do: the compute term is 512 / 480 of the
+    # padded work's (3 splits would be 288 workgroups, 512 / 288); N = 128: 4
+    # tiles, 2 splits, 256 workgroups, one round.
     a70 = dict(B=4, Hq=64, Hkv=8, D=128, n_ctx=131072, elem_bytes=2)
     big_c = dict(bandwidth=1e30, compute_shared=1e15, compute_tiles=1e15, overhead=0.0)
     f96 = 4 * 4 * 8 * 3 * 256 * 131072 * 128
-    w96 = 2 * 4 * 64 * 96 * 3 * 129 * 4
-    assert vo.verify_time_plan(N=96, **a70, **big_c) == pytest.approx(512 / 288 * f96 / 1e15 + w96 / 1e30, rel=1e-12)
+    w96 = 2 * 4 * 64 * 96 * 5 * 129 * 4
+    assert vo.verify_time_plan(N=96, **a70, **big_c) == pytest.approx(512 / 480 * f96 / 1e15 + w96 / 1e30, rel=1e-12)
     f128 = 4 * 4 * 8 * 4 * 256 * 131072 * 128
     assert vo.verify_time_plan(N=128, **a70, **big_c) == pytest.approx(f128 / 1e15, rel=1e-12)
-    assert vo.verify_time_plan(N=128, **a70, **big_c) < vo.verify_time_plan(N=96, **a70, **big_c)
+    assert vo.verify_time_plan(N=96, **a70, **big_c) < vo.verify_time_plan(N=128, **a70, **big_c)
 
 
 def test_controller_stops_at_the_first_decrease():
