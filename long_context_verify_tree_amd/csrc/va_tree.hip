@@ -9,11 +9,13 @@
 //
 // One workgroup per sequence: the candidates are ranked per position in LDS
 // (rank = number of better candidates, ties to the lower index), then one
-// wavefront runs the expansion over an LDS frontier (at most 2N + 1
-// entries), taking each step's best entry with DPP wavefront maxima over
-// 64-bit keys (rho bits, then the earlier parent, then the better rank).
+// wavefront runs the expansion with the frontier in its registers, taking
+// each step's best entry with DPP wavefront maxima over 64-bit keys (rho
+// bits, then the earlier parent, then the better rank).
 
 #include <stdint.h>
+
+#include <type_traits>
 
 #include <hip/hip_runtime.h>
 
@@ -39,6 +41,15 @@ __device__ inline uint32_t wave_max_u32(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 
+// f(integral_constant<int, P>) for P = P0 .. S - 1, each a separate instance
+template <int P0, int S, class F>
+__device__ inline __attribute__((always_inline)) void for_phases(F& f) {
+  if constexpr (P0 < S) {
+    f(std::integral_constant<int, P0>{});
+    for_phases<P0 + 1, S>(f);
+  }
+}
+
 __device__ inline uint64_t entry_key(float rho, int par, int rank) {
   return ((uint64_t)__float_as_uint(rho) << 32) | ((uint64_t)(0xFFFFu - (uint32_t)(par + 1)) << 16) |
          (uint64_t)(0xFFFFu - (uint32_t)rank);
@@ -48,10 +59,7 @@ __global__ __launch_bounds__(kTreeThreads) void tree_kernel(TreeParams p) {
   __shared__ float praw[kTreeMaxKT];
   __shared__ float q[kTreeMaxKT];        // [k][rank], descending per position
   __shared__ int qt[kTreeMaxKT];
-  __shared__ uint64_t fkey[2 * kTreeMaxN + 1];
-  __shared__ int fpar[2 * kTreeMaxN + 1], frank[2 * kTreeMaxN + 1], fdepth[2 * kTreeMaxN + 1];
-  __shared__ float frho[2 * kTreeMaxN + 1];   // rho of the entry's parent (1 for the root)
-  __shared__ int opar[kTreeMaxN], otok[kTreeMaxN];
+  __shared__ int opar[kTreeMaxN], otix[kTreeMaxN];   // parent; candidate (position * T + rank)
   __shared__ float orho[kTreeMaxN];
 
   const int tid = threadIdx.x;
@@ -75,77 +83,115 @@ __global__ __launch_bounds__(kTreeThreads) void tree_kernel(TreeParams p) {
   }
   __syncthreads();
 
+  // Expansion by wavefront 0.  The frontier holds, for each stream (the
+  // root's candidates and then each added node's), its next candidate not
+  // yet taken: node n's children are stream n + 1, taken in rank order, so
+  // a step advances the winner's stream to its next rank (the "next
+  // sibling") and opens the new node's stream at rank 0 (its "best child").
+  // Stream s lives in lane s % 64, slot s / 64, with its head's 64-bit key
+  // and its parent's rho, depth and rank; every lane keeps its best head.
+  // The loop is unrolled over the slot that new streams open in, so every
+  // register index is a compile-time constant and each update is a select.
   if (tid < 64) {
     const int lane = tid;
-    int nf = 1;
-    if (lane == 0) {
-      fkey[0] = entry_key(q[0], -1, 0);
-      fpar[0] = -1;
-      frank[0] = 0;
-      fdepth[0] = 1;
-      frho[0] = 1.f;
+    constexpr int S = (kTreeMaxN + 1 + 63) / 64;   // slots per lane (streams <= N + 1)
+    uint32_t khi[S], klo[S];   // head key (0: no candidate left)
+    float srho[S];             // rho of the stream's parent (1 for the root)
+    int sdep[S], srank[S];     // the parent's depth (candidates at that position); head rank
+#pragma unroll
+    for (int t = 0; t < S; ++t) {
+      khi[t] = klo[t] = 0u;
+      srho[t] = 0.f;
+      sdep[t] = srank[t] = 0;
     }
-    __builtin_amdgcn_wave_barrier();
-    for (int n = 0; n < N; ++n) {
-      uint64_t best = 0;
-      int bi = 0;
-      for (int i = lane; i < nf; i += 64) {
-        const uint64_t k = fkey[i];
-        if (k > best) {
-          best = k;
-          bi = i;
-        }
-      }
-      // the winner: largest rho bits, then the largest tie bits among those
-      // (keys are unique), then the lane that holds it
-      const uint32_t hi = wave_max_u32((uint32_t)(best >> 32));
-      const uint32_t lo = wave_max_u32((uint32_t)(best >> 32) == hi ? (uint32_t)best : 0u);
-      const uint64_t owner = __ballot((uint32_t)(best >> 32) == hi && (uint32_t)best == lo);
-      bi = __builtin_amdgcn_readlane(bi, (int)__builtin_ctzll(owner));
-      // every lane holds the same winner; read it and take the same steps
-      const int par = fpar[bi], rank = frank[bi], depth = fdepth[bi];
-      const float rho_par = frho[bi];
-      const float r = rho_par * q[(depth - 1) * T + rank];
-      __builtin_amdgcn_wave_barrier();
-      if (lane == 0) {
-        opar[n] = par;
-        otok[n] = qt[(depth - 1) * T + rank];
-        orho[n] = r;
-        fkey[bi] = 0;
-      }
-      if (depth < K) {   // best child
-        if (lane == 0) {
-          fkey[nf] = entry_key(r * q[depth * T], n, 0);
-          fpar[nf] = n;
-          frank[nf] = 0;
-          fdepth[nf] = depth + 1;
-          frho[nf] = r;
-        }
-        ++nf;
-      }
-      if (rank + 1 < T) {   // next sibling
-        if (lane == 0) {
-          fkey[nf] = entry_key(rho_par * q[(depth - 1) * T + rank + 1], par, rank + 1);
-          fpar[nf] = par;
-          frank[nf] = rank + 1;
-          fdepth[nf] = depth;
-          frho[nf] = rho_par;
-        }
-        ++nf;
-      }
-      __builtin_amdgcn_wave_barrier();
+    if (lane == 0) {   // stream 0: the root's candidates, best first
+      const uint64_t k0 = entry_key(q[0], -1, 0);
+      khi[0] = (uint32_t)(k0 >> 32);
+      klo[0] = (uint32_t)k0;
+      srho[0] = 1.f;
     }
+    // this lane's best head over slots 0..last
+    uint32_t bh = 0u, bl = 0u;
+    int bsid = 0, bdep = 0, brank = 0;
+    float brho = 0.f;
+    auto rescan = [&](auto last_tag) __attribute__((always_inline)) {
+      constexpr int LAST = decltype(last_tag)::value;
+      bh = bl = 0u;
+#pragma unroll
+      for (int t = 0; t <= LAST; ++t) {
+        const bool better = khi[t] > bh || (khi[t] == bh && klo[t] > bl);
+        bh = better ? khi[t] : bh;
+        bl = better ? klo[t] : bl;
+        bsid = better ? 64 * t + lane : bsid;
+        bdep = better ? sdep[t] : bdep;
+        brank = better ? srank[t] : brank;
+        brho = better ? srho[t] : brho;
+      }
+    };
+    rescan(std::integral_constant<int, 0>{});
+    int n = 0;
+    auto phase = [&](auto phase_tag) __attribute__((always_inline)) {
+      constexpr int P = decltype(phase_tag)::value;
+      // phase P: the new node's stream n + 1 opens in slot P
+      while (n < N && ((n + 1) >> 6) == P) {
+        // the winner: largest rho bits, then the largest tie bits among
+        // those (keys are unique), then the lane that holds it
+        const uint32_t hi = wave_max_u32(bh);
+        const uint64_t cand = __ballot(bh == hi);
+        int owner;
+        if (__builtin_popcountll(cand) > 1) {
+          const uint32_t lo = wave_max_u32(bh == hi ? bl : 0u);
+          owner = (int)__builtin_ctzll(__ballot(bh == hi && bl == lo));
+        } else {
+          owner = (int)__builtin_ctzll(cand);
+        }
+        const int w = __builtin_amdgcn_readlane(bsid, owner);      // winning stream
+        const int dp = __builtin_amdgcn_readlane(bdep, owner);     // its parent's depth
+        const int r = __builtin_amdgcn_readlane(brank, owner);     // the candidate's rank
+        const float rp = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(brho), owner));
+        const float rho_n = __uint_as_float(hi);                   // rp * q[dp][r], as keyed
+        const bool adv = r + 1 < T, child = dp + 1 < K;
+        const float qa = adv ? q[dp * T + r + 1] : 0.f;
+        const float qc = child ? q[(dp + 1) * T] : 0.f;
+        if (lane == 0) {
+          opar[n] = w - 1;
+          orho[n] = rho_n;
+          otix[n] = dp * T + r;
+        }
+        // the winner's stream moves to its next rank
+        const uint64_t ka = adv ? entry_key(rp * qa, w - 1, r + 1) : 0ull;
+        const bool mine = lane == (w & 63);
+#pragma unroll
+        for (int t = 0; t <= P; ++t) {
+          const bool sel = mine && t == (w >> 6);
+          khi[t] = sel ? (uint32_t)(ka >> 32) : khi[t];
+          klo[t] = sel ? (uint32_t)ka : klo[t];
+          srank[t] = sel ? r + 1 : srank[t];
+        }
+        // the new node's stream opens at its best child
+        const uint64_t kc = child ? entry_key(rho_n * qc, n, 0) : 0ull;
+        const bool opens = lane == ((n + 1) & 63);
+        khi[P] = opens ? (uint32_t)(kc >> 32) : khi[P];
+        klo[P] = opens ? (uint32_t)kc : klo[P];
+        srho[P] = opens ? rho_n : srho[P];
+        sdep[P] = opens ? dp + 1 : sdep[P];
+        srank[P] = opens ? 0 : srank[P];
+        rescan(std::integral_constant<int, P>{});
+        ++n;
+      }
+    };
+    for_phases<0, S>(phase);
     if (lane == 0) {
       float a = 0.f;
-      for (int n = 0; n < N; ++n) a += orho[n];
+      for (int m = 0; m < N; ++m) a += orho[m];
       p.a_hat[b] = a;
     }
   }
   __syncthreads();
-  for (int n = tid; n < N; n += kTreeThreads) {
-    p.parent[(int64_t)b * N + n] = opar[n];
-    p.token[(int64_t)b * N + n] = otok[n];
-    p.rho[(int64_t)b * N + n] = orho[n];
+  for (int m = tid; m < N; m += kTreeThreads) {
+    p.parent[(int64_t)b * N + m] = opar[m];
+    p.token[(int64_t)b * N + m] = qt[otix[m]];
+    p.rho[(int64_t)b * N + m] = orho[m];
   }
 }
 
