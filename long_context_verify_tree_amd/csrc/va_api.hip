@@ -112,7 +112,11 @@ va::Plan make_plan(const va_attn_desc* d, int32_t n_ctx) {
   const int64_t target_groups = VA_TARGET_GROUPS;
   const int64_t s0 = pairs < target_groups ? (target_groups + pairs - 1) / pairs : 1;
   int64_t best_len = VA_MIN_SPLIT, best_splits = 0, best_cost = -1;
-  for (int64_t s = 1; s <= 2 * s0 && n_ctx > 0; ++s) {
+  // from ceil(n_ctx / min split) on, every count makes the same minimum-length
+  // splits: the search stops there (the choice is unchanged)
+  const int64_t s_cap = (n_ctx + VA_MIN_SPLIT - 1) / VA_MIN_SPLIT;
+  const int64_t s_end = 2 * s0 < s_cap ? 2 * s0 : s_cap;
+  for (int64_t s = 1; s <= s_end && n_ctx > 0; ++s) {
     int64_t len = (n_ctx + s - 1) / s;
     len = (len + 127) / 128 * 128;
     if (len < VA_MIN_SPLIT) len = VA_MIN_SPLIT;
