@@ -27,9 +27,12 @@ def out_to_f64(t: torch.Tensor) -> np.ndarray:
 
 
 def check_rows(got, ref, got_lse, ref_lse, dtype, what=""):
-    """Tolerances.  fp32: per row max|g-o| <= 1e-5 max|o|, lse relative 1e-5.
-    bf16 (fp32 accumulation): |g-o| <= 2e-2 absolute, plus a normwise check per
-    (b, h) slab (max|g-o| <= 2e-2 max|o|) and |lse_g - lse_o| <= 1e-3."""
+    """Tolerances.  fp32: per row max|g-o| <= 1e-5 max|o|, lse within 1e-5 of
+    max(|lse|, 1): its rounding comes from the fp32 scores (products summed
+    over D, of magnitude ~ sqrt(D) scale for unit inputs), not from how close
+    the lse itself lands to 0.  bf16 (fp32 accumulation): |g-o| <= 2e-2
+    absolute, plus a normwise check per (b, h) slab (max|g-o| <= 2e-2 max|o|)
+    and |lse_g - lse_o| <= 1e-3."""
     got = np.asarray(got, np.float64)
     ref = np.asarray(ref, np.float64)
     assert got.shape == ref.shape, (got.shape, ref.shape)
@@ -40,7 +43,7 @@ def check_rows(got, ref, got_lse, ref_lse, dtype, what=""):
         bad = err.max(axis=-1) > 1e-5 * row_scale
         assert not bad.any(), f"{what}: fp32 rel err {float((err.max(-1) / row_scale).max()):.3e}"
         lerr = np.abs(got_lse - ref_lse)
-        assert (lerr <= 1e-5 * np.abs(ref_lse) + 1e-7).all(), f"{what}: lse err {lerr.max():.3e}"
+        assert (lerr <= 1e-5 * np.maximum(np.abs(ref_lse), 1.0)).all(), f"{what}: lse err {lerr.max():.3e}"
     else:
         assert err.max() <= 2e-2, f"{what}: abs err {err.max():.3e}"
         slab = ref.reshape(-1, ref.shape[-2] * ref.shape[-1]) if ref.ndim >= 2 else ref[None]
