@@ -110,7 +110,11 @@ typedef struct va_attn_desc {
 } va_attn_desc;
 
 /* Workspace bytes needed by verify_attn_dense (n_ctx = L) or
- * verify_attn_sparse (n_ctx = K).  *bytes is set on VA_OK. */
+ * verify_attn_sparse (n_ctx = K).  *bytes is set on VA_OK.  A dense and a
+ * sparse call of one shape and n_ctx may cut the work differently (bf16
+ * with 33..64 query rows per KV head: one 64-row tile per KV head in a
+ * dense call, two 32-row tiles in a sparse one); the workspace holds room
+ * for either cut, so the size does not depend on the mode. */
 va_status va_attn_workspace_size(const va_attn_desc* desc, int32_t n_ctx, size_t* bytes);
 
 /* Dense verification: context part over every cached token [0, L).
@@ -168,7 +172,9 @@ va_status verify_attn_sparse(const va_attn_desc* desc,
  * (verify_idx == NULL: dense over [0, L) and K is ignored; otherwise sparse
  * over the K indices); verify_attn_merge joins them into out / lse.  The
  * merge must be given the same desc and ws and n_ctx = L (dense) or K
- * (sparse), and must run after the partials on the stream. */
+ * (sparse), and must run after the partials on the stream: where the dense
+ * and sparse cuts of the shape join different part counts, it reads the
+ * count the partials wrote into ws. */
 va_status verify_attn_partials(const va_attn_desc* desc,
                                const void* q, const void* k_cache, const void* v_cache,
                                const void* k_draft, const void* v_draft,
@@ -210,10 +216,11 @@ va_status build_draft_tree(const float* cand_prob, const int32_t* cand_token, in
  *
  * va_verify_time_model: T_verify(N) in seconds for desc's shape with N draft
  * nodes over n_ctx context keys, following the plan this library runs (the
- * pages' model is "calibrated by observed execution times"; its structure
- * here is the kernels'): with R = (Hq / Hkv) N query rows per KV head cut
- * into row tiles of `rows` rows (256 in the shared-tile kernel: bf16 with
- * R > 64; else 32, or 64 for float32 with R > 32) and the context cut into
+ * pages fit the model's constants to measured run times; its structure
+ * here is the kernels', those of a dense call): with R = (Hq / Hkv) N query
+ * rows per KV head cut into row tiles of `rows` rows (256 in the shared-tile
+ * kernel: bf16 with R > 64; else 64 when R > 32, else 32) and the context
+ * cut into
  * the call's splits (parts = splits + 1 for the tree, or splits when the
  * shared-tile kernel walks the tree with the last split),
  *     T = max(KV / bandwidth, Q F_pad / compute_k) + W / bandwidth + overhead

@@ -78,18 +78,26 @@ bool overlaps(const void* a, int64_t na, const void* b, int64_t nb) {
   return x < y + (uintptr_t)nb && y < x + (uintptr_t)na;
 }
 
-va::Plan make_plan(const va_attn_desc* d, int32_t n_ctx) {
+// The work cut of one call (kernel, row tiles, splits, parts), which
+// depends on whether the call is dense or sparse.
+va::Plan plan_cut(const va_attn_desc* d, int32_t n_ctx, bool sparse) {
   va::Plan pl{};
   const int G = d->Hq / d->Hkv;
   const int R = G * d->N;
   // bf16 with more than 64 query rows per KV head: the shared-tile rows
-  // kernel (256 rows per workgroup); other bf16 shapes: 32-row tiles (the
-  // row tiles of one split share that XCD's L2 and run in the same round,
-  // so K/V still come from HBM about once); fp32: 32 or 64 rows.
+  // kernel (256 rows per workgroup).  bf16 with 33 to 64 rows: in a dense
+  // call one 64-row tile (two row blocks per wavefront, one wavefront per
+  // SIMD), so each streamed K/V row feeds 64 rows in one workgroup; in a
+  // sparse call two 32-row tiles, as the gathered rows are bound by load
+  // latency and the 64-row tile keeps half as many wavefronts loading.
+  // Other bf16 shapes: 32-row tiles.  fp32: 32 or 64 rows.
 #ifndef VA_ROWS_MIN_R
 #define VA_ROWS_MIN_R 64
 #endif
-  pl.rb = (d->dtype == VA_BF16 && R > VA_ROWS_MIN_R) ? va::kRowsKernel : (d->dtype == VA_BF16 || R <= 32 ? 1 : 2);
+  if (d->dtype == VA_BF16)
+    pl.rb = R > VA_ROWS_MIN_R ? va::kRowsKernel : (R > 32 && !sparse ? 2 : 1);
+  else
+    pl.rb = R <= 32 ? 1 : 2;
   const int rows_per_tile = pl.rb == va::kRowsKernel ? 256 : 32 * pl.rb;
   pl.row_tiles = (R + rows_per_tile - 1) / rows_per_tile;
   const int64_t pairs = (int64_t)d->B * d->Hkv * pl.row_tiles;
@@ -138,9 +146,22 @@ va::Plan make_plan(const va_attn_desc* d, int32_t n_ctx) {
   pl.tree_in_last = pl.rb == va::kRowsKernel && pl.n_ctx_splits > 0;
   pl.n_parts = pl.n_ctx_splits + (pl.tree_in_last ? 0 : 1);
   pl.rows = (int64_t)d->B * d->Hq * d->N;
-  const size_t o_bytes = (size_t)pl.rows * pl.n_parts * d->D * sizeof(float);
+  return pl;
+}
+
+// The plan of a call, with the workspace layout shared by both modes: the
+// workspace query, the partials and a merge called on its own see the same
+// offsets whichever mode ran.  Layout: partial rows [rows][part_stride][D]
+// float32, their log2-sum-exps [rows][part_stride], then a 256-byte header
+// whose first int32 is the part count the partial kernels used.
+va::Plan make_plan(const va_attn_desc* d, int32_t n_ctx, bool sparse) {
+  va::Plan pl = plan_cut(d, n_ctx, sparse);
+  const int other = plan_cut(d, n_ctx, !sparse).n_parts;
+  pl.part_stride = pl.n_parts > other ? pl.n_parts : other;
+  const size_t o_bytes = (size_t)pl.rows * pl.part_stride * d->D * sizeof(float);
   pl.off_lse = align_up(o_bytes);
-  pl.ws_bytes = pl.off_lse + align_up((size_t)pl.rows * pl.n_parts * sizeof(float));
+  pl.off_hdr = pl.off_lse + align_up((size_t)pl.rows * pl.part_stride * sizeof(float));
+  pl.ws_bytes = pl.off_hdr + 256;
   return pl;
 }
 
@@ -161,7 +182,7 @@ va_status run_partials(const va_attn_desc* d, const void* q, const void* kc, con
   if (n_ctx > 0 && (!kc || !vc)) return fail(VA_EINVAL, "k_cache and v_cache must be non-NULL when L > 0");
   if (misaligned(q) || misaligned(kc) || misaligned(vc) || misaligned(kd) || misaligned(vd))
     return fail(VA_EINVAL, "tensor base pointers must be 16-byte aligned");
-  const va::Plan pl = make_plan(d, n_ctx);
+  const va::Plan pl = make_plan(d, n_ctx, sparse);
   if (ws_bytes < pl.ws_bytes || ws == nullptr)
     return fail(VA_EWORKSPACE, "workspace of %zu bytes needed, %zu given", pl.ws_bytes, ws ? ws_bytes : (size_t)0);
   const int64_t groups = (int64_t)d->B * d->Hkv * pl.row_tiles * pl.n_parts;
@@ -186,6 +207,7 @@ va_status run_partials(const va_attn_desc* d, const void* q, const void* kc, con
   }
   p.part_o = (float*)ws;
   p.part_lse = (float*)((char*)ws + pl.off_lse);
+  p.hdr = (int*)((char*)ws + pl.off_hdr);
   p.B = d->B;
   p.Hq = d->Hq;
   p.Hkv = d->Hkv;
@@ -198,6 +220,7 @@ va_status run_partials(const va_attn_desc* d, const void* q, const void* kc, con
   p.split_len = pl.split_len;
   p.n_ctx_splits = pl.n_ctx_splits;
   p.n_parts = pl.n_parts;
+  p.part_stride = pl.part_stride;
   p.tree_in_last = pl.tree_in_last;
   p.total_groups = (int)groups;
   p.c = eff_scale(d) * 1.4426950408889634f;
@@ -206,14 +229,17 @@ va_status run_partials(const va_attn_desc* d, const void* q, const void* kc, con
   return ok();
 }
 
+// mode: 0 after dense partials, 1 after sparse ones, -1 unknown (a merge
+// called on its own: when the two modes' plans join different part counts,
+// the kernel reads the count from the header the partial kernels wrote)
 va_status run_merge(const va_attn_desc* d, int32_t n_ctx, void* out, float* lse, const void* ws, size_t ws_bytes,
-                    hipStream_t stream) {
+                    int mode, hipStream_t stream) {
   va_status st = check_desc(d);
   if (st != VA_OK) return st;
   if (n_ctx < 0 || n_ctx > d->L) return fail(VA_EINVAL, "n_ctx = %d outside [0, L]", n_ctx);
   if (!out) return fail(VA_EINVAL, "out must be non-NULL");
   if (misaligned(out)) return fail(VA_EINVAL, "out must be 16-byte aligned");
-  const va::Plan pl = make_plan(d, n_ctx);
+  const va::Plan pl = make_plan(d, n_ctx, mode == 1);
   if (ws_bytes < pl.ws_bytes || ws == nullptr)
     return fail(VA_EWORKSPACE, "workspace of %zu bytes needed, %zu given", pl.ws_bytes, ws ? ws_bytes : (size_t)0);
   va::MergeParams m{};
@@ -225,7 +251,12 @@ va_status run_merge(const va_attn_desc* d, int32_t n_ctx, void* out, float* lse,
   m.rows = pl.rows;
   m.Hq = d->Hq;
   m.N = d->N;
-  m.n_parts = pl.n_parts;
+  if (mode >= 0)
+    m.n_parts = pl.n_parts;
+  else
+    m.n_parts = plan_cut(d, n_ctx, true).n_parts == pl.n_parts ? pl.n_parts : 0;
+  m.part_stride = pl.part_stride;
+  m.hdr = (const int*)((const char*)ws + pl.off_hdr);
   hipError_t e = va::launch_merge(m, d->dtype, d->D, stream);
   if (e != hipSuccess) return fail(VA_EHIP, "merge kernel launch: %s", hipGetErrorString(e));
   return ok();
@@ -281,7 +312,7 @@ va_status verify_attn_dense_noalloc(const va_attn_desc* desc, const void* q, con
   if (st != VA_OK) return st;
   if (!out) return fail(VA_EINVAL, "out must be non-NULL");
   if (misaligned(out)) return fail(VA_EINVAL, "out must be 16-byte aligned");
-  const size_t need = make_plan(desc, desc->L).ws_bytes;
+  const size_t need = make_plan(desc, desc->L, false).ws_bytes;
   if (need > kScratchBytes)
     return fail(VA_EWORKSPACE, "this shape needs %zu bytes of partials, beyond the fixed scratch of %zu bytes "
                 "(use verify_attn_dense with a caller workspace)", need, kScratchBytes);
@@ -293,7 +324,7 @@ va_status verify_attn_dense_noalloc(const va_attn_desc* desc, const void* q, con
   st = run_partials(desc, q, k_cache, v_cache, k_draft, v_draft, parent, false, nullptr, desc->L, 0, ws,
                     kScratchBytes, (hipStream_t)stream);
   if (st != VA_OK) return st;
-  return run_merge(desc, desc->L, out, lse, ws, kScratchBytes, (hipStream_t)stream);
+  return run_merge(desc, desc->L, out, lse, ws, kScratchBytes, 0, (hipStream_t)stream);
 }
 
 size_t va_noalloc_scratch_bytes(void) { return kScratchBytes; }
@@ -303,7 +334,7 @@ va_status va_attn_workspace_size(const va_attn_desc* desc, int32_t n_ctx, size_t
   if (st != VA_OK) return st;
   if (bytes == nullptr) return fail(VA_EINVAL, "bytes is NULL");
   if (n_ctx < 0 || n_ctx > desc->L) return fail(VA_EINVAL, "n_ctx = %d outside [0, L]", n_ctx);
-  *bytes = make_plan(desc, n_ctx).ws_bytes;
+  *bytes = make_plan(desc, n_ctx, false).ws_bytes;   // the same layout for either mode
   return ok();
 }
 
@@ -317,7 +348,7 @@ va_status verify_attn_partials(const va_attn_desc* desc, const void* q, const vo
 
 va_status verify_attn_merge(const va_attn_desc* desc, int32_t n_ctx, void* out, float* lse, const void* ws,
                             size_t ws_bytes, void* stream) {
-  return run_merge(desc, n_ctx, out, lse, ws, ws_bytes, (hipStream_t)stream);
+  return run_merge(desc, n_ctx, out, lse, ws, ws_bytes, -1, (hipStream_t)stream);
 }
 
 va_status verify_attn_dense(const va_attn_desc* desc, const void* q, const void* k_cache, const void* v_cache,
@@ -330,7 +361,7 @@ va_status verify_attn_dense(const va_attn_desc* desc, const void* q, const void*
   st = run_partials(desc, q, k_cache, v_cache, k_draft, v_draft, parent, false, nullptr, desc->L, 0, ws, ws_bytes,
                     (hipStream_t)stream);
   if (st != VA_OK) return st;
-  return run_merge(desc, desc->L, out, lse, ws, ws_bytes, (hipStream_t)stream);
+  return run_merge(desc, desc->L, out, lse, ws, ws_bytes, 0, (hipStream_t)stream);
 }
 
 va_status verify_attn_sparse(const va_attn_desc* desc, const void* q, const void* k_cache, const void* v_cache,
@@ -344,7 +375,7 @@ va_status verify_attn_sparse(const va_attn_desc* desc, const void* q, const void
   st = run_partials(desc, q, k_cache, v_cache, k_draft, v_draft, parent, true, verify_idx, K, idx_stride, ws,
                     ws_bytes, (hipStream_t)stream);
   if (st != VA_OK) return st;
-  return run_merge(desc, K, out, lse, ws, ws_bytes, (hipStream_t)stream);
+  return run_merge(desc, K, out, lse, ws, ws_bytes, 1, (hipStream_t)stream);
 }
 
 va_status va_select_workspace_size(int32_t B, int32_t L, size_t* bytes) {
@@ -572,7 +603,7 @@ va_status va_verify_time_model(const va_attn_desc* desc, int32_t n_ctx, const va
     return fail(VA_EINVAL, "bandwidth and compute rates must be > 0, overhead >= 0");
   va_attn_desc d = *desc;
   d.N = N;
-  const va::Plan pl = make_plan(&d, n_ctx);
+  const va::Plan pl = make_plan(&d, n_ctx, false);   // a dense call's plan
   const double e = desc->dtype == VA_BF16 ? 2.0 : 4.0;
   const double B = desc->B, Hq = desc->Hq, Hkv = desc->Hkv, D = desc->D, L = n_ctx;
   const double rows = pl.rb == va::kRowsKernel ? 256.0 : 32.0 * pl.rb;

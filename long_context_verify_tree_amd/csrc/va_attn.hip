@@ -145,6 +145,7 @@ void partial_kernel(PartialParams p) {
   // ---- which work item
   int rt, part, kvh, b;
   decode_group(p, rt, part, kvh, b);
+  if (blockIdx.x == 0 && tid == 0) *p.hdr = p.n_parts;   // for a merge called on its own
   const bool tree = part == p.n_ctx_splits;
   const int row0 = rt * 32 * RB;
 
@@ -557,7 +558,7 @@ void partial_kernel(PartialParams p) {
     const int64_t prow = ((int64_t)b * p.Hq + kvh * p.G + g) * p.N + i;
     const float l = l_run[rb];
     const float inv = l > 0.f ? 1.f / l : 0.f;
-    float* dst = p.part_o + (prow * p.n_parts + part) * D;
+    float* dst = p.part_o + (prow * p.part_stride + part) * D;
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
 #pragma unroll
@@ -570,7 +571,7 @@ void partial_kernel(PartialParams p) {
         *(float4*)(dst + 32 * db + 8 * q4 + 4 * h) = v;
       }
     }
-    if (h == 0) p.part_lse[prow * p.n_parts + part] = l > 0.f ? m_all[rb] * c + log2f(l) : -INFINITY;
+    if (h == 0) p.part_lse[prow * p.part_stride + part] = l > 0.f ? m_all[rb] * c + log2f(l) : -INFINITY;
   }
 }
 
@@ -623,6 +624,7 @@ void rows_kernel(PartialParams p) {
 
   int rt, part, kvh, b;
   decode_group(p, rt, part, kvh, b);
+  if (blockIdx.x == 0 && tid == 0) *p.hdr = p.n_parts;   // for a merge called on its own
   // tree: a part of the draft tree alone (no context); tree_after: the last
   // context split, which walks the draft tree after its context keys
   const bool tree = part == p.n_ctx_splits;
@@ -918,7 +920,7 @@ void rows_kernel(PartialParams p) {
     const int g = myrow / p.N, i = myrow % p.N;
     const int64_t prow = ((int64_t)b * p.Hq + kvh * p.G + g) * p.N + i;
     const float inv = l > 0.f ? 1.f / l : 0.f;
-    float* dst = p.part_o + (prow * p.n_parts + part) * D;
+    float* dst = p.part_o + (prow * p.part_stride + part) * D;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -927,7 +929,7 @@ void rows_kernel(PartialParams p) {
                                o[db][4 * q4 + 3] * inv);
         *(float4*)(dst + 32 * db + 8 * q4 + 4 * h) = v;
       }
-    if (h == 0) p.part_lse[prow * p.n_parts + part] = l > 0.f ? m_run * c + log2f(l) : -INFINITY;
+    if (h == 0) p.part_lse[prow * p.part_stride + part] = l > 0.f ? m_run * c + log2f(l) : -INFINITY;
   }
 }
 
@@ -962,7 +964,10 @@ __device__ inline MergeRow merge_row(const MergeParams& p, int64_t prow) {
 // joined group by group with the running maximum rescaled, as in the partial
 // kernels.  (Several rows per wavefront gained at most 7% on 32k rows and
 // lost 19% on 3.6k rows, where too few workgroups were left.)
-template <class T, int D, int MG>
+// HDR: the part count is read from the header the partial kernels wrote
+// (a merge called on its own after a shape whose dense and sparse plans
+// join different part counts), kept inside the workspace's slots.
+template <class T, int D, int MG, bool HDR>
 __global__ __launch_bounds__(256) void merge_kernel(MergeParams p) {
   constexpr int PER = D / 64;
   const int lane = threadIdx.x & 63;
@@ -970,9 +975,9 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeParams p) {
   if (prow_l >= p.rows) return;
   const int64_t prow = (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(prow_l >> 32)) << 32) |
                                  (uint32_t)__builtin_amdgcn_readfirstlane((int)prow_l));
-  const int np = p.n_parts;
-  const float* lse2 = p.part_lse + prow * np;
-  const float* po = p.part_o + prow * np * D + lane * PER;
+  const int np = HDR ? min(max(*p.hdr, 1), p.part_stride) : p.n_parts;
+  const float* lse2 = p.part_lse + prow * p.part_stride;
+  const float* po = p.part_o + prow * p.part_stride * D + lane * PER;
 
   float m_run = -INFINITY, wsum = 0.f;
   float acc[PER];
@@ -1091,7 +1096,11 @@ hipError_t launch_partials(const PartialParams& p, int dtype, int D, int rb, boo
 
 template <class T, int D>
 void launch_merge_d(const MergeParams& p, hipStream_t stream) {
-  hipLaunchKernelGGL((merge_kernel<T, D, 16>), dim3((unsigned)((p.rows + 3) / 4)), dim3(256), 0, stream, p);
+  const dim3 grid((unsigned)((p.rows + 3) / 4));
+  if (p.n_parts == 0)
+    hipLaunchKernelGGL((merge_kernel<T, D, 16, true>), grid, dim3(256), 0, stream, p);
+  else
+    hipLaunchKernelGGL((merge_kernel<T, D, 16, false>), grid, dim3(256), 0, stream, p);
 }
 
 hipError_t launch_merge(const MergeParams& p, int dtype, int D, hipStream_t stream) {

@@ -16,9 +16,13 @@ namespace va {
 // Keys: the n_ctx context keys are cut into n_ctx_splits splits of
 // split_len keys; the draft (tree) keys form one more part.  Every
 // (sequence, kv head, row tile, part) is one workgroup that writes one
-// normalised partial output and its log2-sum-exp.
+// normalised partial output and its log2-sum-exp.  The plan of a dense call
+// can differ from that of a sparse call of the same shape and n_ctx; the
+// workspace layout cannot (it holds part_stride partial slots per row, the
+// larger of the two part counts, and a header with the part count the
+// partial kernels used).
 // Plan::rb value selecting rows_kernel (bf16, many query rows per KV head:
-// 256 rows per workgroup, 64 per wavefront, K/V tiles shared in LDS).
+// 256 rows per workgroup, 32 per wavefront, K/V tiles shared in LDS).
 constexpr int kRowsKernel = 8;
 
 struct Plan {
@@ -28,8 +32,10 @@ struct Plan {
   int n_ctx_splits;  // ceil(n_ctx / split_len); 0 when n_ctx == 0
   int n_parts;       // n_ctx_splits + 1 (the tree part is last), or n_ctx_splits when tree_in_last
   int tree_in_last;  // the shared-tile kernel's last split also walks the draft tree
+  int part_stride;   // partial slots per row in the workspace (either mode's n_parts fits)
   int64_t rows;      // B * Hq * N output rows
   size_t off_lse;    // byte offset of the partial lse array in the workspace
+  size_t off_hdr;    // byte offset of the header (int32 n_parts written by the partial kernels)
   size_t ws_bytes;   // total workspace bytes
 };
 
@@ -43,11 +49,12 @@ struct PartialParams {
   const int32_t* idx;   // verify set (sparse) or nullptr (dense)
   int64_t idx_stride;
   int64_t qs[3], kcs[3], vcs[3], kds[3], vds[3];
-  float* part_o;        // [rows][n_parts][D]
-  float* part_lse;      // [rows][n_parts], log2 domain
+  float* part_o;        // [rows][part_stride][D], slots [0, n_parts) written
+  float* part_lse;      // [rows][part_stride], log2 domain
+  int* hdr;             // workspace header: n_parts, written by workgroup 0
   int B, Hq, Hkv, G, N, L, n_ctx;
   int R;                // G * N
-  int row_tiles, split_len, n_ctx_splits, n_parts;
+  int row_tiles, split_len, n_ctx_splits, n_parts, part_stride;
   int tree_in_last;     // no tree part: the last context split walks the tree too
   int total_groups;     // grid size
   float c;              // scale * log2(e)
@@ -60,7 +67,10 @@ struct MergeParams {
   float* lse;           // may be nullptr
   int64_t os[3];
   int64_t rows;
-  int Hq, N, n_parts;
+  int Hq, N;
+  int n_parts;          // parts to join, or 0: read them from hdr (clamped to [1, part_stride])
+  int part_stride;      // partial slots per row
+  const int* hdr;       // workspace header written by the partial kernels
 };
 
 struct CommitParams {

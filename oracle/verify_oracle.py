@@ -456,11 +456,12 @@ def verify_time_model(B: int, Hq: int, Hkv: int, D: int, n_ctx: int, N: int, ele
     return max(nbytes / bandwidth, flops / compute) + overhead
 
 
-def kernel_plan(B: int, Hq: int, Hkv: int, n_ctx: int, N: int, elem_bytes: int):
+def kernel_plan(B: int, Hq: int, Hkv: int, n_ctx: int, N: int, elem_bytes: int, sparse: bool = False):
     """How the verification library cuts one call into work (its documented
     plan, restated here): the G * N query rows of a KV head go in row tiles
     of 256 rows (the shared-tile kernel, bf16 with more than 64 rows), else
-    32 rows (bf16), else 32 or 64 rows (fp32, 64 when more than 32 rows);
+    for bf16 one 64-row tile (33 to 64 rows in a dense call) or 32-row tiles,
+    else 32 or 64 rows (fp32, 64 when more than 32 rows);
     the context keys go in splits of a multiple of 128 keys (at least 512),
     their count chosen for the soonest end of the context workgroups' rounds
     on a 256-CU device running one workgroup per CU.
@@ -472,7 +473,9 @@ def kernel_plan(B: int, Hq: int, Hkv: int, n_ctx: int, N: int, elem_bytes: int):
     shared = elem_bytes == 2 and R > 64
     if shared:
         rows = 256
-    elif elem_bytes == 2 or R <= 32:
+    elif elem_bytes == 2:
+        rows = 64 if R > 32 and not sparse else 32
+    elif R <= 32:
         rows = 32
     else:
         rows = 64

@@ -242,12 +242,15 @@ def test_controller_host_functions_match_the_oracle(ops):
             got = ops.verify_time_model(d, n_ctx, bw, cs, ct, c0, N)
             want = vo.verify_time_plan(shape["B"], shape["Hq"], shape["Hkv"], shape["D"], n_ctx, N, e, bw, cs, ct, c0)
             assert got == pytest.approx(want, rel=1e-12), (shape, n_ctx, N)
-            # and the parts of that plan are the library's (its workspace size)
+            # and the parts of the plans are the library's (its workspace size:
+            # slots for the larger of the dense and sparse part counts, then a
+            # 256-byte header)
             d.N = N
             _, ws = ws_size(ops, d, n_ctx)
             rows = shape["B"] * shape["Hq"] * N
-            parts = vo.kernel_plan(shape["B"], shape["Hq"], shape["Hkv"], n_ctx, N, e)[4]
-            assert ws == -(-rows * parts * shape["D"] * 4 // 256) * 256 + -(-rows * parts * 4 // 256) * 256
+            parts = max(vo.kernel_plan(shape["B"], shape["Hq"], shape["Hkv"], n_ctx, N, e, sparse=sp)[4]
+                        for sp in (False, True))
+            assert ws == -(-rows * parts * shape["D"] * 4 // 256) * 256 + -(-rows * parts * 4 // 256) * 256 + 256
             d.N = 8
     for _ in range(50):
         n = int(rng.integers(1, 40))

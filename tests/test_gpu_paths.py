@@ -43,9 +43,10 @@ def run_sparse(ops, x, idx):
 
 
 def n_parts(ops, x, n_ctx):
-    """Parts the library's plan joins (context splits + the tree part), read
-    back from the workspace size: rows * parts * (D + 1) floats, each array
-    rounded up to 256 bytes."""
+    """Partial slots per row of the library's workspace (the larger of the
+    dense and sparse plans' part counts: context splits + the tree part),
+    read back from the workspace size: rows * parts * (D + 1) floats, each
+    array rounded up to 256 bytes, and a 256-byte header."""
     d = device_inputs(x)
     out = torch.empty_like(d["q"])
     desc = ops.make_desc(d["q"], d["k_cache"], d["v_cache"], d["k_draft"], d["v_draft"], out)
@@ -83,6 +84,51 @@ def test_merge_across_groups_peaky_late_split(gpu_lib):
     ref, rlse = vo.verify_attention(x.q, x.k_cache, x.v_cache, x.k_draft, x.v_draft, x.parent)
     check_rows(got, ref, glse, rlse, cfg.dtype, "merge33late")
     assert np.abs(ref).max() > 0.3
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_dense_and_sparse_plans_on_one_workspace(gpu_lib, D):
+    # bf16 with 56 query rows per KV head: a dense call runs one 64-row tile
+    # per KV head (the per-wavefront kernel's bf16 two-row-block instance), a
+    # sparse call two 32-row tiles, and the two plans join different part
+    # counts.  Partials of either mode, each followed by a merge called on its
+    # own (it reads the part count the partials wrote into the workspace
+    # header), alternate on one workspace; then the one-call entry points.
+    cfg = cfg_of(f"modes_D{D}", B=2, Hq=14, Hkv=2, D=D, L=5000, N=8, tree="uniform", seed=1500 + D)
+    x = synth.make_inputs(cfg)
+    rng = np.random.default_rng(D)
+    K = 1700
+    idx = np.stack([np.sort(rng.permutation(cfg.L)[:K]) for _ in range(cfg.B)]).astype(np.int32)
+    pd = vo.kernel_plan(cfg.B, cfg.Hq, cfg.Hkv, cfg.L, cfg.N, 2)
+    ps = vo.kernel_plan(cfg.B, cfg.Hq, cfg.Hkv, K, cfg.N, 2, sparse=True)
+    say(f"case dense/sparse plans D={D}: dense {pd}, sparse {ps}")
+    assert pd[1:3] == (64, 1) and ps[1:3] == (32, 2) and pd[4] != ps[4]
+    refs = {
+        "dense": vo.verify_attention(x.q, x.k_cache, x.v_cache, x.k_draft, x.v_draft, x.parent),
+        "sparse": vo.verify_attention(x.q, x.k_cache, x.v_cache, x.k_draft, x.v_draft, x.parent, ctx_index=idx),
+    }
+    d = device_inputs(x)
+    it = torch.from_numpy(idx).cuda()
+    out = torch.empty_like(d["q"])
+    lse = torch.empty(cfg.B, cfg.Hq, cfg.N, dtype=torch.float32, device="cuda")
+    desc = gpu_lib.make_desc(d["q"], d["k_cache"], d["v_cache"], d["k_draft"], d["v_draft"], out)
+    ws = torch.empty(max(gpu_lib.workspace_size(desc, cfg.L), gpu_lib.workspace_size(desc, K)), dtype=torch.uint8,
+                     device="cuda")
+    for mode in ("sparse", "dense", "sparse", "dense"):
+        say(f"case dense/sparse plans D={D}: {mode} partials, merge on its own")
+        out.fill_(float("nan"))
+        sp = mode == "sparse"
+        gpu_lib.verify_attn_partials(desc, d["q"], d["k_cache"], d["v_cache"], d["k_draft"], d["v_draft"],
+                                     d["parent"], ws, verify_idx=it if sp else None)
+        gpu_lib.verify_attn_merge(desc, K if sp else cfg.L, out, lse, ws)
+        torch.cuda.synchronize()
+        ref, rlse = refs[mode]
+        check_rows(out_to_f64(out), ref, lse.cpu().numpy().astype(np.float64), rlse, cfg.dtype, f"{cfg.name}/{mode}")
+    say(f"case dense/sparse plans D={D}: one-call entry points")
+    got, glse = run_dense(gpu_lib, x)
+    check_rows(got, *refs["dense"][:1], glse, refs["dense"][1], cfg.dtype, cfg.name + "/dense call")
+    got, glse = run_sparse(gpu_lib, x, idx)
+    check_rows(got, *refs["sparse"][:1], glse, refs["sparse"][1], cfg.dtype, cfg.name + "/sparse call")
 
 
 @pytest.mark.parametrize("L", [0, 100, 1111])

@@ -78,7 +78,7 @@ def test_random_shape_matches_oracle(gpu_lib, case):
     x = synth.make_inputs(cfg)
     n_ctx = c["K"] if c["K"] is not None else c["L"]
     es = 2 if c["dtype"] == synth.BF16 else 4
-    plan = vo.kernel_plan(cfg.B, cfg.Hq, cfg.Hkv, n_ctx, cfg.N, es)
+    plan = vo.kernel_plan(cfg.B, cfg.Hq, cfg.Hkv, n_ctx, cfg.N, es, sparse=c["K"] is not None)
     say(f"case sweep {case_id(c)}: shared-tile kernel {plan[0]}, row tiles {plan[2]}, splits {plan[3]}, "
         f"parts {plan[4]}")
     d = device_inputs(x)

@@ -845,9 +845,20 @@ def test_kernel_plan_hand_cases():
     # from the plan rules.  N = 8: 32 rows, one 32-row tile, 64 (b, kvh)
     # pairs -> 4 splits of 8192 keys
     assert vo.kernel_plan(8, 32, 8, 32768, 8, 2) == (False, 32, 1, 4, 5)
-    # N = 16: 64 rows, still the per-wavefront kernel, two 32-row tiles ->
-    # 128 pairs -> 2 splits of 16384
-    assert vo.kernel_plan(8, 32, 8, 32768, 16, 2) == (False, 32, 2, 2, 3)
+    # N = 16: 64 rows, still the per-wavefront kernel.  Dense: one 64-row
+    # tile -> 64 pairs; rounds x keys per split for 1..8 splits: 1 x 32768,
+    # 1 x 16384, 1 x 11008 (3 x 11008 keys, 192 workgroups), 1 x 8192, then
+    # 2 x 6656, 2 x 5504, 2 x 4736, 2 x 4096 -> 4 splits of 8192.  Sparse:
+    # two 32-row tiles -> 128 pairs -> 2 splits of 16384
+    assert vo.kernel_plan(8, 32, 8, 32768, 16, 2) == (False, 64, 1, 4, 5)
+    assert vo.kernel_plan(8, 32, 8, 32768, 16, 2, sparse=True) == (False, 32, 2, 2, 3)
+    # 33 rows: the same split between the modes; 32 rows: 32-row tiles in both
+    assert vo.kernel_plan(1, 33, 1, 4096, 1, 2)[1:3] == (64, 1)
+    assert vo.kernel_plan(1, 33, 1, 4096, 1, 2, sparse=True)[1:3] == (32, 2)
+    assert vo.kernel_plan(1, 32, 1, 4096, 1, 2, sparse=True)[1:3] == vo.kernel_plan(1, 32, 1, 4096, 1, 2)[1:3] == (32, 1)
+    # the shared-tile and fp32 plans do not depend on the mode
+    assert vo.kernel_plan(4, 64, 8, 4096, 128, 2, sparse=True) == vo.kernel_plan(4, 64, 8, 4096, 128, 2)
+    assert vo.kernel_plan(1, 8, 1, 256, 7, 4, sparse=True) == vo.kernel_plan(1, 8, 1, 256, 7, 4)
     # N = 17: 68 rows -> the shared-tile kernel, one 256-row tile; its last
     # split walks the tree, so the parts are the splits
     assert vo.kernel_plan(8, 32, 8, 32768, 17, 2) == (True, 256, 1, 4, 4)
