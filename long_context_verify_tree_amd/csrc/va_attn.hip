@@ -1057,16 +1057,19 @@ hipError_t launch_p(const PartialParams& p, hipStream_t stream) {
 }
 
 // The non-temporal hint goes on dense bf16 reads with one row tile per KV
-// head (each K/V row read once); with several row tiles the later tiles
-// find the rows in L2.
+// head (each K/V row read once), of 32 or 64 rows; with several row tiles
+// the later tiles find the rows in L2.
 template <class T, int D>
 hipError_t launch_p_rb(const PartialParams& p, int rb, bool gather, hipStream_t stream) {
+  const bool nt = sizeof(T) == 2 && !gather && p.row_tiles == 1;
   if (rb == 1) {
     if (gather) return launch_p<T, D, 1, true>(p, stream);
-    if (sizeof(T) == 2 && p.row_tiles == 1) return launch_p<T, D, 1, false, true>(p, stream);
+    if (nt) return launch_p<T, D, 1, false, true>(p, stream);
     return launch_p<T, D, 1, false>(p, stream);
   }
-  return gather ? launch_p<T, D, 2, true>(p, stream) : launch_p<T, D, 2, false>(p, stream);
+  if (gather) return launch_p<T, D, 2, true>(p, stream);
+  if (nt) return launch_p<T, D, 2, false, true>(p, stream);
+  return launch_p<T, D, 2, false>(p, stream);
 }
 
 template <int D, bool G>
