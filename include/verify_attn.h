@@ -113,8 +113,10 @@ typedef struct va_attn_desc {
  * verify_attn_sparse (n_ctx = K).  *bytes is set on VA_OK.  A dense and a
  * sparse call of one shape and n_ctx may cut the work differently (bf16
  * with 33..64 query rows per KV head: one 64-row tile per KV head in a
- * dense call, two 32-row tiles in a sparse one); the workspace holds room
- * for either cut, so the size does not depend on the mode. */
+ * dense call, two 32-row tiles in a sparse one; the tree walked by the last
+ * context split in a dense call that fills the chip, in its own workgroups
+ * in a sparse one); the workspace holds room for either cut, so the size
+ * does not depend on the mode. */
 va_status va_attn_workspace_size(const va_attn_desc* desc, int32_t n_ctx, size_t* bytes);
 
 /* Dense verification: context part over every cached token [0, L).
@@ -167,8 +169,10 @@ va_status verify_attn_sparse(const va_attn_desc* desc,
 /* The two stages that verify_attn_dense / verify_attn_sparse enqueue, for
  * callers that time or schedule them separately.  verify_attn_partials
  * writes the split context partials and the tree partial into ws (the
- * shared-tile kernel, when the context has splits, walks the tree in the
- * same workgroup as the last split and writes no separate tree partial)
+ * last context split walks the tree after its context keys, and no
+ * separate tree partial is written, in the shared-tile kernel whenever the
+ * context has splits, and in a dense call whose context workgroups number
+ * at least 256)
  * (verify_idx == NULL: dense over [0, L) and K is ignored; otherwise sparse
  * over the K indices); verify_attn_merge joins them into out / lse.  The
  * merge must be given the same desc and ws and n_ctx = L (dense) or K
@@ -220,9 +224,9 @@ va_status build_draft_tree(const float* cand_prob, const int32_t* cand_token, in
  * here is the kernels', those of a dense call): with R = (Hq / Hkv) N query
  * rows per KV head cut into row tiles of `rows` rows (256 in the shared-tile
  * kernel: bf16 with R > 64; else 64 when R > 32, else 32) and the context
- * cut into
- * the call's splits (parts = splits + 1 for the tree, or splits when the
- * shared-tile kernel walks the tree with the last split),
+ * cut into the call's splits (parts = splits + 1 for the tree, or splits when the
+ * last split walks the tree: in the shared-tile kernel, or when the
+ * context workgroups number at least 256),
  *     T = max(KV / bandwidth, Q F_pad / compute_k) + W / bandwidth + overhead
  * KV = 2 B Hkv n_ctx D e, F_pad = 4 B Hkv tiles rows n_ctx D (padded rows
  * included), compute_k = compute_shared or compute_tiles by kernel,

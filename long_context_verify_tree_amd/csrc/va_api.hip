@@ -141,9 +141,14 @@ va::Plan plan_cut(const va_attn_desc* d, int32_t n_ctx, bool sparse) {
   // The shared-tile kernel runs one workgroup per CU: the tree rides on the
   // last context split's workgroup (after its context keys), so the grid is
   // the context workgroups alone and each row has one partial row fewer.
-  // The per-wavefront kernels keep the tree as a part of its own (short
-  // workgroups that start first).
-  pl.tree_in_last = pl.rb == va::kRowsKernel && pl.n_ctx_splits > 0;
+  // The per-wavefront kernels do the same in a dense call whose context
+  // workgroups fill the chip (otherwise a tree workgroup of its own runs
+  // beside them on an idle CU); in a sparse call they keep the tree as a
+  // part of its own (short workgroups that start first): the gathered
+  // kernel runs two workgroups per CU, so its tree workgroups displace no
+  // context workgroup.
+  const bool fills = pairs * pl.n_ctx_splits >= target_groups;
+  pl.tree_in_last = pl.n_ctx_splits > 0 && (pl.rb == va::kRowsKernel || (!sparse && fills));
   pl.n_parts = pl.n_ctx_splits + (pl.tree_in_last ? 0 : 1);
   pl.rows = (int64_t)d->B * d->Hq * d->N;
   return pl;

@@ -147,6 +147,9 @@ void partial_kernel(PartialParams p) {
   decode_group(p, rt, part, kvh, b);
   if (blockIdx.x == 0 && tid == 0) *p.hdr = p.n_parts;   // for a merge called on its own
   const bool tree = part == p.n_ctx_splits;
+  // the last context split of a call whose tree rides on it walks the draft
+  // tree after its context keys (dense calls only: no gathered instance)
+  const bool tree_after = !GATHER && p.tree_in_last && part == p.n_ctx_splits - 1;
   const int row0 = rt * 32 * RB;
 
   auto q_row_ptr = [&](int r) __attribute__((always_inline)) -> const T* {
@@ -154,27 +157,33 @@ void partial_kernel(PartialParams p) {
     return (const T*)p.q + (int64_t)b * p.qs[0] + (int64_t)(kvh * p.G + g) * p.qs[1] + (int64_t)i * p.qs[2];
   };
 
-  // ---- key range of this part and its buffer resources
-  const T* kbase;
-  const T* vbase;
+  // ---- key range of the walk (this part's context keys, or the draft
+  // tree) and its buffer resources
   uint32_t kts_b, vts_b;     // bytes between consecutive keys
-  int ke, region;            // keys of the part; keys addressable in the region
-  if (tree) {
-    kbase = (const T*)p.kd + (int64_t)b * p.kds[0] + (int64_t)kvh * p.kds[1];
-    vbase = (const T*)p.vd + (int64_t)b * p.vds[0] + (int64_t)kvh * p.vds[1];
-    kts_b = (uint32_t)(p.kds[2] * ES);
-    vts_b = (uint32_t)(p.vds[2] * ES);
-    ke = region = p.N;
-  } else {
-    kbase = (const T*)p.kc + (int64_t)b * p.kcs[0] + (int64_t)kvh * p.kcs[1];
-    vbase = (const T*)p.vc + (int64_t)b * p.vcs[0] + (int64_t)kvh * p.vcs[1];
-    kts_b = (uint32_t)(p.kcs[2] * ES);
-    vts_b = (uint32_t)(p.vcs[2] * ES);
-    ke = p.n_ctx;
-    region = p.L;
-  }
-  const rsrc_t krs = make_rsrc(kbase, (uint32_t)region * kts_b);
-  const rsrc_t vrs = make_rsrc(vbase, (uint32_t)region * vts_b);
+  int ke;                    // keys of the walk
+  rsrc_t krs, vrs;
+  auto set_region = [&](bool tr) __attribute__((always_inline)) {
+    const T* kbase;
+    const T* vbase;
+    int region;              // keys addressable in the region
+    if (tr) {
+      kbase = (const T*)p.kd + (int64_t)b * p.kds[0] + (int64_t)kvh * p.kds[1];
+      vbase = (const T*)p.vd + (int64_t)b * p.vds[0] + (int64_t)kvh * p.vds[1];
+      kts_b = (uint32_t)(p.kds[2] * ES);
+      vts_b = (uint32_t)(p.vds[2] * ES);
+      ke = region = p.N;
+    } else {
+      kbase = (const T*)p.kc + (int64_t)b * p.kcs[0] + (int64_t)kvh * p.kcs[1];
+      vbase = (const T*)p.vc + (int64_t)b * p.vcs[0] + (int64_t)kvh * p.vcs[1];
+      kts_b = (uint32_t)(p.kcs[2] * ES);
+      vts_b = (uint32_t)(p.vcs[2] * ES);
+      ke = p.n_ctx;
+      region = p.L;
+    }
+    krs = make_rsrc(kbase, (uint32_t)region * kts_b);
+    vrs = make_rsrc(vbase, (uint32_t)region * vts_b);
+  };
+  set_region(tree);
   const bool gather = GATHER && !tree;
   const rsrc_t irs = make_rsrc(GATHER ? p.idx + (int64_t)b * p.idx_stride : p.idx, GATHER ? (uint32_t)p.n_ctx * 4u : 0u);
   const int ntiles = ke > 0 ? (ke + kTileKeys - 1) / kTileKeys : 0;
@@ -440,7 +449,7 @@ void partial_kernel(PartialParams p) {
 
   // ---- ancestor bitmasks of the draft tree, one per row of this tile.
   // Ctx parts fill them with ones so the mask lookup needs no branch.
-  if (tree) {
+  auto build_anc = [&]() __attribute__((always_inline)) {
     for (int j = tid; j < p.N; j += kThreads) par[j] = p.parent[(int64_t)b * p.N + j];
     for (int j = tid; j < 32 * RB * kAncWords; j += kThreads) (&anc[0][0])[j] = 0u;
     __syncthreads();
@@ -452,10 +461,14 @@ void partial_kernel(PartialParams p) {
         j = (pj >= -1 && pj < j) ? pj : -1;  // malformed parents end the path
       }
     }
+    __syncthreads();
+  };
+  if (tree) {
+    build_anc();
   } else {
     for (int j = tid; j < 32 * RB * kAncWords; j += kThreads) (&anc[0][0])[j] = ~0u;
+    __syncthreads();
   }
-  __syncthreads();
 
   // Stage ring slot pp in the wavefront's LDS tile; with reload, re-issue
   // each chunk for tile tn right after it is staged.
@@ -504,6 +517,23 @@ void partial_kernel(PartialParams p) {
     if (k + pp < nw) {
       stage(pp, false, 0);
       compute(tile_of(k + pp), vmask[pp], std::true_type{});
+    }
+  }
+  if constexpr (!GATHER) {
+    if (tree_after) {
+      // the draft tree's (at most 8) tiles, continuing each wavefront's
+      // running softmax: tile t goes to wavefront t mod 4, one at a time
+      // through the first ring slot (once every wavefront is done with the
+      // all-ones mask of its context tiles)
+      __syncthreads();
+      build_anc();
+      set_region(true);
+      for (int t = wave; t < (ke + kTileKeys - 1) / kTileKeys; t += kWaves) {
+        load_tile(t, 0, kreg[0], vreg[0]);
+        const uint32_t vm = tile_mask(t, 0);
+        stage(0, false, 0);
+        compute(t, vm, std::true_type{});
+      }
     }
   }
 
@@ -975,7 +1005,6 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeParams p) {
   if (prow_l >= p.rows) return;
   const int64_t prow = (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(prow_l >> 32)) << 32) |
                                  (uint32_t)__builtin_amdgcn_readfirstlane((int)prow_l));
-  const int np = HDR ? min(max(*p.hdr, 1), p.part_stride) : p.n_parts;
   const float* lse2 = p.part_lse + prow * p.part_stride;
   const float* po = p.part_o + prow * p.part_stride * D + lane * PER;
 
@@ -983,41 +1012,36 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeParams p) {
   float acc[PER];
 #pragma unroll
   for (int e = 0; e < PER; ++e) acc[e] = 0.f;
-  for (int s0 = 0; s0 < np; s0 += MG) {
-    const int cnt = min(MG, np - s0);
-    float lv[MG], v[MG][PER];
+  // part slot s of this row into (lv, v)
+  auto load_slot = [&](int s, float& lv, float (&v)[PER]) __attribute__((always_inline)) {
+    lv = lse2[s];
+    const float* src = po + (int64_t)s * D;
+    if constexpr (PER == 2) {
+      const float2 t = *(const float2*)src;
+      v[0] = t.x;
+      v[1] = t.y;
+    } else {
 #pragma unroll
-    for (int u = 0; u < MG; ++u) {
-      lv[u] = -INFINITY;
-#pragma unroll
-      for (int e = 0; e < PER; ++e) v[u][e] = 0.f;
-      if (u < cnt) {   // uniform: only the parts that exist are loaded
-        lv[u] = lse2[s0 + u];
-        const float* src = po + (int64_t)(s0 + u) * D;
-        if constexpr (PER == 2) {
-          const float2 t = *(const float2*)src;
-          v[u][0] = t.x;
-          v[u][1] = t.y;
-        } else {
-#pragma unroll
-          for (int e = 0; e < PER; ++e) v[u][e] = src[e];
-        }
-      }
+      for (int e = 0; e < PER; ++e) v[e] = src[e];
     }
+  };
+  // join the first cnt of G loaded parts into the running (m_run, wsum, acc)
+  auto join = [&](auto g_tag, int cnt, bool first, const float* lv, const float (*v)[PER]) __attribute__((always_inline)) {
+    constexpr int G = decltype(g_tag)::value;
     float gm = -INFINITY;
 #pragma unroll
-    for (int u = 0; u < MG; ++u)
+    for (int u = 0; u < G; ++u)
       if (u < cnt) gm = fmaxf(gm, lv[u]);
     const float mnew = fmaxf(m_run, gm);
     const float muse = mnew == -INFINITY ? 0.f : mnew;
-    if (s0 > 0) {
+    if (!first) {
       const float alpha = m_run == -INFINITY ? 0.f : exp2f(m_run - muse);
       wsum *= alpha;
 #pragma unroll
       for (int e = 0; e < PER; ++e) acc[e] *= alpha;
     }
 #pragma unroll
-    for (int u = 0; u < MG; ++u) {
+    for (int u = 0; u < G; ++u) {
       if (u < cnt) {
         const float w = exp2f(lv[u] - muse);
         wsum += w;
@@ -1026,6 +1050,41 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeParams p) {
       }
     }
     m_run = mnew;
+  };
+  if constexpr (HDR) {
+    // The part count comes from the header the partial kernels wrote (kept
+    // inside the workspace's slots).  The slots are loaded before it is
+    // known, with indices clamped to the last slot, in groups of 8 (a slot
+    // past the part count is loaded but not used), so the header's latency
+    // overlaps the loads.
+    constexpr int GH = 8;
+    const int hv = *p.hdr;
+    const int last = p.part_stride - 1;
+    float lv[GH], v[GH][PER];
+#pragma unroll
+    for (int u = 0; u < GH; ++u) load_slot(min(u, last), lv[u], v[u]);
+    __builtin_amdgcn_sched_barrier(0);   // the header's first use after the loads
+    const int np = min(max(hv, 1), p.part_stride);
+    join(std::integral_constant<int, GH>{}, min(GH, np), true, lv, v);
+    for (int s0 = GH; s0 < np; s0 += GH) {
+#pragma unroll
+      for (int u = 0; u < GH; ++u) load_slot(min(s0 + u, last), lv[u], v[u]);
+      join(std::integral_constant<int, GH>{}, min(GH, np - s0), false, lv, v);
+    }
+  } else {
+    const int np = p.n_parts;
+    for (int s0 = 0; s0 < np; s0 += MG) {
+      const int cnt = min(MG, np - s0);
+      float lv[MG], v[MG][PER];
+#pragma unroll
+      for (int u = 0; u < MG; ++u) {
+        lv[u] = -INFINITY;
+#pragma unroll
+        for (int e = 0; e < PER; ++e) v[u][e] = 0.f;
+        if (u < cnt) load_slot(s0 + u, lv[u], v[u]);   // uniform: only the parts that exist
+      }
+      join(std::integral_constant<int, MG>{}, cnt, s0 == 0, lv, v);
+    }
   }
   const MergeRow mr = merge_row(p, prow);
   const float muse = m_run == -INFINITY ? 0.f : m_run;

@@ -465,10 +465,11 @@ def kernel_plan(B: int, Hq: int, Hkv: int, n_ctx: int, N: int, elem_bytes: int, 
     the context keys go in splits of a multiple of 128 keys (at least 512),
     their count chosen for the soonest end of the context workgroups' rounds
     on a 256-CU device running one workgroup per CU.
-    The tree is one more part, except in the shared-tile kernel, whose last
-    context split walks the tree after its context keys (one part when there
-    is no context).  Returns (shared_tile_kernel, rows per tile, row tiles
-    per KV head, context splits, parts)."""
+    The tree is one more part, except where the last context split walks
+    the tree after its context keys: in the shared-tile kernel, and in a
+    dense call whose context workgroups number at least 256 (one part when
+    there is no context).  Returns (shared_tile_kernel, rows per tile, row
+    tiles per KV head, context splits, parts)."""
     R = (Hq // Hkv) * N
     shared = elem_bytes == 2 and R > 64
     if shared:
@@ -493,7 +494,8 @@ def kernel_plan(B: int, Hq: int, Hkv: int, n_ctx: int, N: int, elem_bytes: int, 
         cost = -(-(pairs * cnt) // 256) * split
         if best is None or cost < best:
             best, splits = cost, cnt
-    return shared, rows, tiles, splits, splits if shared and splits > 0 else splits + 1
+    folded = splits > 0 and (shared or (not sparse and pairs * splits >= 256))
+    return shared, rows, tiles, splits, splits if folded else splits + 1
 
 
 def verify_time_plan(B: int, Hq: int, Hkv: int, D: int, n_ctx: int, N: int, elem_bytes: int,

@@ -843,14 +843,18 @@ def test_time_model_regimes_and_ridge():
 def test_kernel_plan_hand_cases():
     # Llama-3-8B layer shape (G = 4), batch 8, 32768 keys, bf16: worked by hand
     # from the plan rules.  N = 8: 32 rows, one 32-row tile, 64 (b, kvh)
-    # pairs -> 4 splits of 8192 keys
-    assert vo.kernel_plan(8, 32, 8, 32768, 8, 2) == (False, 32, 1, 4, 5)
+    # pairs -> 4 splits of 8192 keys.  Its 256 context workgroups fill the
+    # chip, so a dense call's last split walks the tree (4 parts); a sparse
+    # call keeps the tree part (5)
+    assert vo.kernel_plan(8, 32, 8, 32768, 8, 2) == (False, 32, 1, 4, 4)
+    assert vo.kernel_plan(8, 32, 8, 32768, 8, 2, sparse=True) == (False, 32, 1, 4, 5)
     # N = 16: 64 rows, still the per-wavefront kernel.  Dense: one 64-row
     # tile -> 64 pairs; rounds x keys per split for 1..8 splits: 1 x 32768,
     # 1 x 16384, 1 x 11008 (3 x 11008 keys, 192 workgroups), 1 x 8192, then
-    # 2 x 6656, 2 x 5504, 2 x 4736, 2 x 4096 -> 4 splits of 8192.  Sparse:
-    # two 32-row tiles -> 128 pairs -> 2 splits of 16384
-    assert vo.kernel_plan(8, 32, 8, 32768, 16, 2) == (False, 64, 1, 4, 5)
+    # 2 x 6656, 2 x 5504, 2 x 4736, 2 x 4096 -> 4 splits of 8192, 256
+    # workgroups, the tree folded into the last.  Sparse: two 32-row tiles ->
+    # 128 pairs -> 2 splits of 16384, and the tree part
+    assert vo.kernel_plan(8, 32, 8, 32768, 16, 2) == (False, 64, 1, 4, 4)
     assert vo.kernel_plan(8, 32, 8, 32768, 16, 2, sparse=True) == (False, 32, 2, 2, 3)
     # 33 rows: the same split between the modes; 32 rows: 32-row tiles in both
     assert vo.kernel_plan(1, 33, 1, 4096, 1, 2)[1:3] == (64, 1)
@@ -874,7 +878,8 @@ def test_kernel_plan_hand_cases():
     # (288 workgroups), 2 x 32768, 2 x 26240 (480), 3 x 21888 -> 5 splits
     assert vo.kernel_plan(4, 64, 8, 131072, 96, 2) == (True, 256, 3, 5, 5)
     # 200 pairs (25 sequences, one tile each): 1 to 4 splits all take one
-    # context length in all (1 x L, 2 x L/2, ...) -> the fewest, 1
+    # context length in all (1 x L, 2 x L/2, ...) -> the fewest, 1; 200
+    # context workgroups leave CUs for the tree part, which stays
     assert vo.kernel_plan(25, 32, 8, 32768, 8, 2) == (False, 32, 1, 1, 2)
     # short context: splits never below 512 keys; no context: only the tree part
     assert vo.kernel_plan(1, 4, 1, 700, 8, 2) == (False, 32, 1, 2, 3)
@@ -889,8 +894,9 @@ def test_plan_time_model_closed_forms():
     args = dict(B=8, Hq=32, Hkv=8, D=128, n_ctx=32768, elem_bytes=2)
     bw, cs, ct, c0 = 5e12, 1.2e15, 0.4e15, 4e-6
     kv = 2 * 8 * 8 * 32768 * 128 * 2
-    # N = 8: memory-bound per-wavefront kernel, 5 parts
-    w8 = 2 * 8 * 32 * 8 * 5 * 129 * 4
+    # N = 8: memory-bound per-wavefront kernel, 4 parts (its 256 context
+    # workgroups fill the chip: the tree rides on the last split)
+    w8 = 2 * 8 * 32 * 8 * 4 * 129 * 4
     assert vo.verify_time_plan(N=8, bandwidth=bw, compute_shared=cs, compute_tiles=ct, overhead=c0, **args) == \
         pytest.approx(kv / bw + w8 / bw + c0, rel=1e-12)
     # N = 64: one 256-row tile of the shared-tile kernel (256 rows, no
