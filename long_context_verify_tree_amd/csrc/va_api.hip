@@ -149,6 +149,17 @@ va::Plan plan_cut(const va_attn_desc* d, int32_t n_ctx, bool sparse) {
   // context workgroup.
   const bool fills = pairs * pl.n_ctx_splits >= target_groups;
   pl.tree_in_last = pl.n_ctx_splits > 0 && (pl.rb == va::kRowsKernel || (!sparse && fills));
+  // The shared-tile kernel walks each split as one contiguous key range, so
+  // when its last split also walks the N tree keys, the other splits take
+  // those keys' worth more context: every split then walks about
+  // (n_ctx + N) / S keys (rounded up to whole 32-key tiles), and none more
+  // than before.  (The per-wavefront kernel deals its tiles round-robin
+  // over the splits.)
+  if (pl.tree_in_last && pl.rb == va::kRowsKernel && pl.n_ctx_splits > 1) {
+    const int64_t S = pl.n_ctx_splits;
+    const int64_t len = ((n_ctx + (int64_t)d->N + S - 1) / S + 31) / 32 * 32;
+    if (len > pl.split_len && (S - 1) * len < n_ctx) pl.split_len = (int)len;
+  }
   pl.n_parts = pl.n_ctx_splits + (pl.tree_in_last ? 0 : 1);
   pl.rows = (int64_t)d->B * d->Hq * d->N;
   return pl;
