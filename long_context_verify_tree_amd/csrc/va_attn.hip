@@ -10,7 +10,10 @@
 //   partial_kernel  one workgroup per (sequence, kv head, row tile, part).
 //                   Parts 0..S-1 are context splits (dense range or gathered
 //                   verify-set indices, Dustin "Workflow di Verifica");
-//                   part S is the draft tree under its ancestor mask.
+//                   part S is the draft tree under its ancestor mask (in a
+//                   dense call whose context workgroups fill the chip, the
+//                   last context split walks the tree after its context
+//                   keys instead).
 //                   Writes a normalised partial row and its log2-sum-exp.
 //   merge_kernel    one wavefront per output row: log-sum-exp merge of the
 //                   S + 1 partials with wavefront shuffles.

@@ -4,8 +4,9 @@
 // probabilities q_k; a node at depth d picks one candidate at each of the
 // first d positions and scores rho = q_0 * ... * q_{d-1}.  The tree grows by
 // adding, N times, the valid node of highest rho; adding a node makes its
-// best child and its next sibling valid.  Since rho never grows along a
-// path, the result is the N prefixes of largest rho, prefix-closed.
+// best child and its next sibling valid.  With marginals in [0, 1] rho
+// never grows along a path, and the result is the N prefixes of largest
+// rho, prefix-closed (the expansion below follows the rule for any input).
 //
 // One workgroup per sequence: the candidates are ranked per position in LDS
 // (rank = number of better candidates, ties to the lower index), then one
