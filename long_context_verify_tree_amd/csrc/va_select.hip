@@ -339,8 +339,15 @@ constexpr int kRT = 1024;                  // threads per resolve workgroup
 constexpr int kRW = kRT / 64;
 constexpr int kRCap = 8192;                // list entries resolved in LDS
 constexpr int kEPT = kRCap / kRT;          // list entries per thread at most (8)
-constexpr int kSeg = kRT * 32;             // tokens per exact-way segment
-static_assert(kSeg == kSelectSegTokens, "segment size of the length limit");
+// The exact way walks a row in segments of kXQ runs of 4096 tokens (kXQ * 4
+// keys per thread).  Four runs: 16 keys per thread, so that the fallback's
+// registers stay below what the list path needs and the kernel needs no
+// scratch (with eight runs, 32 keys and another 32 for the target tier's
+// draft picks, it spilled and every call paid for it, taken or not).
+constexpr int kXQ = 4;
+constexpr int kXK = 4 * kXQ;               // keys per thread per exact-way segment
+constexpr int kSeg = kRT * kXK;            // tokens per exact-way segment
+static_assert(kSelectSegTokens % kSeg == 0, "the length limit is whole exact-way segments");
 static_assert(kMaxFP <= kRT, "one segment count per thread");
 
 struct RShared {
@@ -453,24 +460,24 @@ __device__ __forceinline__ uint64_t list_select(const uint32_t* key, const int* 
   return sh.pstar;
 }
 
-// The exact way.  A segment of 32768 tokens: thread t holds tokens
-// base + 4096 q + 4 t + e (q < 8, e < 4) as bit 4 q + e; index order is
+// The exact way.  A segment of kSeg tokens: thread t holds tokens
+// base + 4096 q + 4 t + e (q < kXQ, e < 4) as bit 4 q + e; index order is
 // (q, t, e).  Tokens past L read 0 (never candidates).
-__device__ inline void seg_keys(dev::rsrc_t rs, bool vec, const float* row, int base, uint32_t (&key)[32]) {
+__device__ inline void seg_keys(dev::rsrc_t rs, bool vec, const float* row, int base, uint32_t (&key)[kXK]) {
   const int b0 = base + 4 * (int)threadIdx.x;
   if (vec) {
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
+    for (int q = 0; q < kXQ; ++q) {
       const uint4 v = *reinterpret_cast<const uint4*>(row + b0 + q * 4 * kRT);
       key[4 * q + 0] = v.x, key[4 * q + 1] = v.y, key[4 * q + 2] = v.z, key[4 * q + 3] = v.w;
     }
   } else {
 #pragma unroll
-    for (int i = 0; i < 32; ++i)
+    for (int i = 0; i < kXK; ++i)
       key[i] = __builtin_amdgcn_raw_buffer_load_b32(rs, (b0 + (i >> 2) * 4 * kRT + (i & 3)) * 4, 0, 0);
   }
 #pragma unroll
-  for (int i = 0; i < 32; ++i) key[i] = key_of_bits(key[i]);
+  for (int i = 0; i < kXK; ++i) key[i] = key_of_bits(key[i]);
 }
 
 __device__ inline int seg_token(int base, int i) { return base + (i >> 2) * 4 * kRT + 4 * (int)threadIdx.x + (i & 3); }
@@ -479,15 +486,15 @@ __device__ inline uint32_t seg_bits(int base, int lo, int hi) {
   const int b0 = base + 4 * (int)threadIdx.x;
   uint32_t m = 0;
 #pragma unroll
-  for (int q = 0; q < 8; ++q) m |= nib_bits(b0 + q * 4 * kRT, lo, hi) << (4 * q);
+  for (int q = 0; q < kXQ; ++q) m |= nib_bits(b0 + q * 4 * kRT, lo, hi) << (4 * q);
   return m;
 }
 
 // Bits of this thread's tokens whose rank is >= P.
-__device__ inline uint32_t seg_sel(const uint32_t (&key)[32], int base, uint64_t P) {
+__device__ inline uint32_t seg_sel(const uint32_t (&key)[kXK], int base, uint64_t P) {
   uint32_t m = 0;
 #pragma unroll
-  for (int i = 0; i < 32; ++i) m |= (uint32_t)(rank_of(key[i], seg_token(base, i)) >= P) << i;
+  for (int i = 0; i < kXK; ++i) m |= (uint32_t)(rank_of(key[i], seg_token(base, i)) >= P) << i;
   return m;
 }
 
@@ -500,11 +507,11 @@ __device__ uint64_t exact_tier(const SelParams p, const float* row, const float*
   const int L = p.L, nseg = (L + kSeg - 1) / kSeg;
   const dev::rsrc_t rs = dev::make_rsrc(row, (uint32_t)L * 4u), rsd = dev::make_rsrc(drow, (uint32_t)L * 4u);
   const bool al = ((reinterpret_cast<uintptr_t>(row) | reinterpret_cast<uintptr_t>(drow)) & 15u) == 0;
-  uint32_t key[32];
+  uint32_t key[kXK];
   auto cand_of = [&](int s) __attribute__((always_inline)) {
     uint32_t c = seg_bits(s * kSeg, p.lo, p.hi);
     if (target) {
-      uint32_t k2[32];
+      uint32_t k2[kXK];
       seg_keys(rsd, al && (s + 1) * kSeg <= L, drow, s * kSeg, k2);
       c &= ~seg_sel(k2, s * kSeg, pd);
     }
@@ -521,7 +528,7 @@ __device__ uint64_t exact_tier(const SelParams p, const float* row, const float*
       const uint32_t cand = cand_of(s);
       seg_keys(rs, al && (s + 1) * kSeg <= L, row, s * kSeg, key);
 #pragma unroll
-      for (int i = 0; i < 32; ++i)
+      for (int i = 0; i < kXK; ++i)
         if (((cand >> i) & 1u) && (key[i] & fixed) == prefix)
           atomicAdd(&hist[(key[i] >> shift) & (uint32_t)(nb - 1)], 1);
     }
@@ -554,8 +561,8 @@ __device__ uint64_t exact_tier(const SelParams p, const float* row, const float*
     seg_keys(rs, al && (s + 1) * kSeg <= L, row, s * kSeg, key);
     uint32_t eq = 0;
 #pragma unroll
-    for (int i = 0; i < 32; ++i) eq |= (uint32_t)(((cand >> i) & 1u) && key[i] == prefix) << i;
-    for (int q = 0; q < 8; ++q) {   // one scan per run of 4096 tokens
+    for (int i = 0; i < kXK; ++i) eq |= (uint32_t)(((cand >> i) & 1u) && key[i] == prefix) << i;
+    for (int q = 0; q < kXQ; ++q) {   // one scan per run of 4096 tokens
       const uint32_t nbits = (eq >> (4 * q)) & 15u;
       int tot;
       int before = run + block_excl_scan<true, kRW>(__popc(nbits), sh.wsum, &tot);
@@ -579,14 +586,14 @@ __device__ void exact_output(const SelParams p, const float* ds, const float* ts
   const bool al = ((reinterpret_cast<uintptr_t>(ds) | reinterpret_cast<uintptr_t>(ts)) & 15u) == 0;
   int written = 0;
   for (int s = 0; s < nseg; ++s) {
-    uint32_t key[32];
+    uint32_t key[kXK];
     const bool vec = al && (s + 1) * kSeg <= L;
     const uint32_t f = seg_bits(s * kSeg, p.lo, p.hi), valid = seg_bits(s * kSeg, 0, L);
     seg_keys(rsd, vec, ds, s * kSeg, key);
     const uint32_t dsel = f & seg_sel(key, s * kSeg, pd);
     seg_keys(rst, vec, ts, s * kSeg, key);
     const uint32_t sel = (valid & ~f) | dsel | (f & ~dsel & seg_sel(key, s * kSeg, pt));
-    for (int q = 0; q < 8; ++q) {
+    for (int q = 0; q < kXQ; ++q) {
       const uint32_t nbits = (sel >> (4 * q)) & 15u;
       int tot;
       int pos = written + block_excl_scan<true, kRW>(__popc(nbits), sh.wsum, &tot);
