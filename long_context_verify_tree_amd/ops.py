@@ -245,8 +245,13 @@ def verify_attn_partials(desc: AttnDesc, q, k_cache, v_cache, k_draft, v_draft, 
     load()
     K = verify_idx.shape[1] if verify_idx is not None else desc.L
     stride = _row_stride(verify_idx, K) if verify_idx is not None else 0
+    # the library tells a sparse call by a non-NULL index pointer; an empty
+    # [B, 0] list may have none, and with K = 0 no index is read
+    idx_ptr = None
+    if verify_idx is not None:
+        idx_ptr = _ptr(verify_idx) if verify_idx.numel() > 0 else _ptr(workspace)
     _check(_lib.verify_attn_partials(ctypes.byref(desc), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_draft),
-                                     _ptr(v_draft), _ptr(parent), _ptr(verify_idx), K, stride, _ptr(workspace),
+                                     _ptr(v_draft), _ptr(parent), idx_ptr, K, stride, _ptr(workspace),
                                      workspace.numel(), _stream(q.device)))
 
 

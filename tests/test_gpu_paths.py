@@ -193,3 +193,18 @@ def test_sparse_empty_verify_set(gpu_lib, shape):
     got, glse = run_sparse(gpu_lib, x, idx)
     ref, rlse = vo.verify_attention(x.q, x.k_cache, x.v_cache, x.k_draft, x.v_draft, x.parent, ctx_index=idx)
     check_rows(got, ref, glse, rlse, cfg.dtype, f"K=0 {shape}")
+    # the two stages, with an empty index list, after dense partials on the
+    # same workspace
+    say(f"case sparse K=0 {shape}, partials and a merge called on its own")
+    d = device_inputs(x)
+    out = torch.empty_like(d["q"])
+    lse = torch.empty(cfg.B, cfg.Hq, cfg.N, dtype=torch.float32, device="cuda")
+    desc = gpu_lib.make_desc(d["q"], d["k_cache"], d["v_cache"], d["k_draft"], d["v_draft"], out)
+    ws = torch.empty(max(gpu_lib.workspace_size(desc, cfg.L), gpu_lib.workspace_size(desc, 0)), dtype=torch.uint8,
+                     device="cuda")
+    gpu_lib.verify_attn_partials(desc, d["q"], d["k_cache"], d["v_cache"], d["k_draft"], d["v_draft"], d["parent"], ws)
+    gpu_lib.verify_attn_partials(desc, d["q"], d["k_cache"], d["v_cache"], d["k_draft"], d["v_draft"], d["parent"], ws,
+                                 verify_idx=torch.from_numpy(idx).cuda())
+    gpu_lib.verify_attn_merge(desc, 0, out, lse, ws)
+    torch.cuda.synchronize()
+    check_rows(out_to_f64(out), ref, lse.cpu().numpy().astype(np.float64), rlse, cfg.dtype, f"K=0 staged {shape}")
