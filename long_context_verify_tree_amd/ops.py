@@ -243,6 +243,9 @@ def verify_attn_partials(desc: AttnDesc, q, k_cache, v_cache, k_draft, v_draft, 
                          verify_idx=None):
     """First stage only (split partials + tree partial) into ``workspace``."""
     load()
+    if verify_idx is not None and (verify_idx.dtype != torch.int32 or verify_idx.dim() != 2 or
+                                   (verify_idx.shape[1] > 1 and verify_idx.stride(1) != 1)):
+        raise ValueError("verify_idx must be int32 [B, K] with unit column stride")
     K = verify_idx.shape[1] if verify_idx is not None else desc.L
     stride = _row_stride(verify_idx, K) if verify_idx is not None else 0
     # the library tells a sparse call by a non-NULL index pointer; an empty

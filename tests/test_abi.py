@@ -146,6 +146,22 @@ def test_sparse_rejects_before_launch(ops):
     assert sparse(100, 100, ws_bytes=16) == ops.VA_EWORKSPACE
 
 
+def test_staged_partials_binding_checks_the_index_list(ops):
+    # the binding rejects a malformed verify list before any library call
+    # (CPU tensors: nothing reaches a device)
+    import torch
+    q = torch.zeros(1, 4, 8, 64, dtype=torch.bfloat16)
+    kc = torch.zeros(1, 1, 100, 64, dtype=torch.bfloat16)
+    kd = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16)
+    parent = torch.zeros(1, 8, dtype=torch.int32)
+    desc = ops.make_desc(q, kc, kc, kd, kd, q)
+    ws = torch.zeros(16, dtype=torch.uint8)
+    for bad in (torch.zeros(1, 10, dtype=torch.int64), torch.zeros(10, dtype=torch.int32),
+                torch.zeros(1, 20, dtype=torch.int32)[:, ::2]):
+        with pytest.raises(ValueError):
+            ops.verify_attn_partials(desc, q, kc, kc, kd, kd, parent, ws, verify_idx=bad)
+
+
 def select(ops, B, L, ld, sink, window, m, budget, out=FAKE, ds=FAKE, ws=None, ws_bytes=0):
     return ops._lib.select_verify_set(ds, FAKE, B, L, ld, sink, window, m, budget, out, ws, ws_bytes, None)
 
