@@ -15,8 +15,8 @@
 //                   last context split walks the tree after its context
 //                   keys instead).
 //                   Writes a normalised partial row and its log2-sum-exp.
-//   merge_kernel    one wavefront per output row: log-sum-exp merge of the
-//                   S + 1 partials with wavefront shuffles.
+//   merge_kernel    D / 4 lanes per output row (16 bytes of each part per
+//                   lane): log-sum-exp merge of the row's partials.
 //
 // Inside partial_kernel the four wavefronts of a workgroup stream disjoint
 // 32-key tiles (wave w takes tiles w, w+4, ...).  Each tile of K and V is
@@ -989,27 +989,32 @@ __device__ inline MergeRow merge_row(const MergeParams& p, int64_t prow) {
   return m;
 }
 
-// One wavefront per output row, its parts joined MG at a time.  The row's
-// part log2-sum-exps are the same for every lane, so they are read with
-// scalar loads, issued together with the partial-row loads of up to MG parts
-// (one memory round trip per group, no cross-lane reduction); the weights
-// exp2(lse_s - max) then scale the partial rows.  More than MG parts are
-// joined group by group with the running maximum rescaled, as in the partial
-// kernels.  (Several rows per wavefront gained at most 7% on 32k rows and
-// lost 19% on 3.6k rows, where too few workgroups were left.)
+// D / 4 lanes per output row, each holding 16 bytes of every part's row, so
+// a wavefront joins 256 / D rows at once; the parts are joined MG at a time.
+// A lane loads its row's part log2-sum-exps together with its slices of up to
+// MG partial rows (one memory round trip per group, no cross-lane
+// reduction); the weights exp2(lse_s - max) then scale the slices.  More than
+// MG parts are joined group by group with the running maximum rescaled, as
+// in the partial kernels.  The kernel is bound by the round-trip latency of
+// its wavefronts, not by bytes: on 32k rows of two parts, two rows per
+// wavefront (16-byte loads) took 8.5 us where one row per wavefront (8-byte
+// loads, scalar part weights) took 13.7 us; a few thousand rows stay at the
+// launch floor either way.
 // HDR: the part count is read from the header the partial kernels wrote
 // (a merge called on its own after a shape whose dense and sparse plans
 // join different part counts), kept inside the workspace's slots.
 template <class T, int D, int MG, bool HDR>
 __global__ __launch_bounds__(256) void merge_kernel(MergeParams p) {
-  constexpr int PER = D / 64;
+  constexpr int PER = 4;                 // values per lane: 16 bytes of each part's row
+  constexpr int LPR = D / PER;           // lanes per row
+  constexpr int RPW = 64 / LPR;          // rows per wavefront
   const int lane = threadIdx.x & 63;
-  const int64_t prow_l = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (prow_l >= p.rows) return;
-  const int64_t prow = (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(prow_l >> 32)) << 32) |
-                                 (uint32_t)__builtin_amdgcn_readfirstlane((int)prow_l));
+  const int64_t prow = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * RPW + lane / LPR;
+  // no lane of the wavefront talks to another, so a lane past the last row
+  // simply leaves
+  if (prow >= p.rows) return;
   const float* lse2 = p.part_lse + prow * p.part_stride;
-  const float* po = p.part_o + prow * p.part_stride * D + lane * PER;
+  const float* po = p.part_o + prow * p.part_stride * D + (lane % LPR) * PER;
 
   float m_run = -INFINITY, wsum = 0.f;
   float acc[PER];
@@ -1018,15 +1023,11 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeParams p) {
   // part slot s of this row into (lv, v)
   auto load_slot = [&](int s, float& lv, float (&v)[PER]) __attribute__((always_inline)) {
     lv = lse2[s];
-    const float* src = po + (int64_t)s * D;
-    if constexpr (PER == 2) {
-      const float2 t = *(const float2*)src;
-      v[0] = t.x;
-      v[1] = t.y;
-    } else {
-#pragma unroll
-      for (int e = 0; e < PER; ++e) v[e] = src[e];
-    }
+    const float4 t = *(const float4*)(po + (int64_t)s * D);
+    v[0] = t.x;
+    v[1] = t.y;
+    v[2] = t.z;
+    v[3] = t.w;
   };
   // join the first cnt of G loaded parts into the running (m_run, wsum, acc)
   auto join = [&](auto g_tag, int cnt, bool first, const float* lv, const float (*v)[PER]) __attribute__((always_inline)) {
@@ -1092,23 +1093,16 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeParams p) {
   const MergeRow mr = merge_row(p, prow);
   const float muse = m_run == -INFINITY ? 0.f : m_run;
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
-  T* orow = (T*)p.out + mr.b * p.os[0] + (int64_t)mr.hq * p.os[1] + (int64_t)mr.i * p.os[2] + lane * PER;
-  if constexpr (sizeof(T) == 2 && PER == 2) {
-    const uint32_t lo = __builtin_bit_cast(uint16_t, (__bf16)(acc[0] * inv));
-    const uint32_t hi = __builtin_bit_cast(uint16_t, (__bf16)(acc[1] * inv));
-    *(uint32_t*)orow = lo | (hi << 16);
-  } else {
+  T* orow = (T*)p.out + mr.b * p.os[0] + (int64_t)mr.hq * p.os[1] + (int64_t)mr.i * p.os[2] + (lane % LPR) * PER;
+  if constexpr (sizeof(T) == 2) {
+    uint32_t h[PER];
 #pragma unroll
-    for (int e = 0; e < PER; ++e) {
-      const float v = acc[e] * inv;
-      if constexpr (sizeof(T) == 2) {
-        orow[e] = __builtin_bit_cast(uint16_t, (__bf16)v);
-      } else {
-        orow[e] = v;
-      }
-    }
+    for (int e = 0; e < PER; ++e) h[e] = __builtin_bit_cast(uint16_t, (__bf16)(acc[e] * inv));
+    *(uint2*)orow = uint2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
+  } else {
+    *(float4*)orow = float4{acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv};
   }
-  if (p.lse != nullptr && lane == 0)
+  if (p.lse != nullptr && lane % LPR == 0)
     p.lse[prow] = wsum > 0.f ? (muse + log2f(wsum)) * 0.69314718055994530942f : -INFINITY;
 }
 
@@ -1161,11 +1155,12 @@ hipError_t launch_partials(const PartialParams& p, int dtype, int D, int rb, boo
 
 template <class T, int D>
 void launch_merge_d(const MergeParams& p, hipStream_t stream) {
-  const dim3 grid((unsigned)((p.rows + 3) / 4));
+  constexpr int rows_per_group = 4 * (256 / D);   // four wavefronts of 64 / (D / 4) rows
+  const dim3 grid((unsigned)((p.rows + rows_per_group - 1) / rows_per_group));
   if (p.n_parts == 0)
-    hipLaunchKernelGGL((merge_kernel<T, D, 16, true>), grid, dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((merge_kernel<T, D, 8, true>), grid, dim3(256), 0, stream, p);
   else
-    hipLaunchKernelGGL((merge_kernel<T, D, 16, false>), grid, dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((merge_kernel<T, D, 8, false>), grid, dim3(256), 0, stream, p);
 }
 
 hipError_t launch_merge(const MergeParams& p, int dtype, int D, hipStream_t stream) {
