@@ -171,8 +171,10 @@ __global__ __launch_bounds__(256) void score_finish_kernel(ScoreParams p) {
   for (int r = tid; r < R; r += 256) {
     const int64_t row = (int64_t)b * R + r;
     float M = -INFINITY;
+#pragma unroll 8
     for (int sp = 0; sp < p.n_splits; ++sp) M = fmaxf(M, p.stat_m[row * p.n_splits + sp]);
     float l = 0.f;
+#pragma unroll 8
     for (int sp = 0; sp < p.n_splits; ++sp) {
       const float ms = p.stat_m[row * p.n_splits + sp];
       l += ms == -INFINITY ? 0.f : p.stat_l[row * p.n_splits + sp] * fast_exp2(ms - M);
@@ -184,6 +186,9 @@ __global__ __launch_bounds__(256) void score_finish_kernel(ScoreParams p) {
   if (j >= p.L) return;
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
   const float* sb = p.s + (int64_t)b * R * p.ld_s + j;
+  // unrolled so that eight rows' loads are in flight at once (the sum keeps
+  // its row order)
+#pragma unroll 8
   for (int r = 0; r < R; ++r) {
     const float4 v = *(const float4*)(sb + (int64_t)r * p.ld_s);   // rows padded to 32 tokens
     const float z = lse2[r];
