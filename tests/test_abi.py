@@ -278,3 +278,28 @@ def test_controller_host_functions_match_the_oracle(ops):
         ops.verify_time_model(d, 100, 0.0, 1e15, 1e15, 0.0, 4)
     with pytest.raises(ops.VerifyAttnError):
         ops.choose_tree_size(np.ones(3), np.ones(3), 0.0, 0.0)
+
+
+def test_error_messages_are_per_thread(ops):
+    # two host threads fail different calls, then each reads the message of
+    # its own call (the library keeps the last message per thread)
+    import threading
+    bar = threading.Barrier(2)
+    got = {}
+
+    def worker(name, over):
+        d = good_desc(ops)
+        for k, v in over.items():
+            setattr(d, k, v)
+        st = ws_size(ops, d, 100)[0]
+        bar.wait()   # both calls have failed before either message is read
+        got[name] = (st, ops._lib.va_last_error().decode())
+
+    ts = [threading.Thread(target=worker, args=("d", {"D": 96})),
+          threading.Thread(target=worker, args=("h", {"Hq": 6, "Hkv": 4}))]
+    for t in ts:
+        t.start()
+    for t in ts:
+        t.join(timeout=60)
+    assert got["d"][0] == 2 and "D = 96" in got["d"][1]
+    assert got["h"][0] == 1 and "multiple of Hkv" in got["h"][1]
