@@ -66,3 +66,32 @@ def test_calls_follow_the_callers_stream(gpu_lib):
     check_rows(out_to_f64(got[1]), r_s, got[2].cpu().numpy().astype(np.float64), rl_s, cfg.dtype, "side stream sparse")
     r_d, rl_d = vo.verify_attention(x.q, x.k_cache, x.v_cache, x.k_draft, x.v_draft, x.parent)
     check_rows(out_to_f64(got[3]), r_d, got[4].cpu().numpy().astype(np.float64), rl_d, cfg.dtype, "side stream dense")
+
+
+def test_two_streams_with_own_workspaces(gpu_lib):
+    # calls that overlap in time on two streams, each with its own outputs
+    # and workspace, give what the same calls give one after another
+    say("case two streams: two problems, select -> sparse -> dense on each of two side streams at once")
+    probs = []
+    for seed in (606, 707):
+        cfg = synth.VerifyConfig("streams2", B=2, Hq=8, Hkv=2, D=128, L=20000, N=16, tree="uniform",
+                                 dtype=synth.BF16, seed=seed)
+        x = synth.make_inputs(cfg)
+        g = torch.Generator(device="cuda").manual_seed(seed)
+        probs.append((device_inputs(x), torch.rand(cfg.B, cfg.L, device="cuda", generator=g),
+                      torch.rand(cfg.B, cfg.L, device="cuda", generator=g)))
+    ref = [chain(gpu_lib, *p) for p in probs]
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    got = [None, None]
+    for s in streams:
+        s.wait_stream(torch.cuda.current_stream())
+    for rep in range(3):
+        for i, s in enumerate(streams):
+            with torch.cuda.stream(s):
+                got[i] = chain(gpu_lib, *probs[i])
+        for s in streams:
+            s.synchronize()
+        for i in range(2):
+            for name, a, b in zip(("verify_idx", "sparse out", "sparse lse", "dense out", "dense lse"), ref[i], got[i]):
+                assert torch.equal(a, b), f"repeat {rep}, problem {i}: {name} differs from the serial call"
